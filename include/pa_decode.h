@@ -1,0 +1,183 @@
+/*
+ * pa_decode.h -- C ABI of libpa_decode.so: paged single-query decode attention
+ * on AMD MI355X (gfx950).
+ *
+ * The operation.  For every sequence s and query head h, attention of the one
+ * decode-step query q[s][h] over the L = seq_lens[s] cached tokens of s, with
+ * grouped-query heads: query head h reads kv head h / G, G = num_q_heads /
+ * num_kv_heads.
+ *   z_t = scale * (q . k_t),  out = sum_t softmax(z)_t * v_t,   t = 0 .. L-1
+ * Token t of sequence s lives in slot t % 16 of physical block
+ * block_tables[s][t / 16].
+ *
+ * Sources (project_6 commit pages):
+ *   - paged cache read through a per-sequence block id list, 16-token blocks,
+ *     GQA by broadcasting each kv head over its group: commit 15ef28e
+ *     (paged_attention_v2_pytorch.py), message "[OPT] Vectorize
+ *     paged_attention_v2";
+ *   - V1 (one pass over the whole sequence per unit of work) and V2 (Phase 1
+ *     per-partition max logit, exp-sum and partial output; Phase 2 merge with
+ *     the global max and the rescale exp(m_p - M) * s_p): commit 15ef28e,
+ *     message "[OPT] PagedAttention V2 implementation";
+ *   - partition size as the tuning knob (512 vs 1024), and V2 only for
+ *     max_seq_len above 8192: commit 900ae0b (vllm/_custom_ops.py), messages
+ *     "Two changes based on CCCL source reading" and "THE SINGLE
+ *     HIGHEST-IMPACT CODE CHANGE";
+ *   - caller-owned, pre-allocated V2 intermediates: commit 490ff98
+ *     (paged_attn.py), "Three changes", item 2.
+ *
+ * Layouts (row-major, contiguous, all in device memory):
+ *   query, out      [num_seqs][num_q_heads][head_dim]              dtype
+ *   key_cache,
+ *   value_cache     [num_blocks][num_kv_heads][block_size][head_dim] dtype
+ *   block_tables    [num_seqs][max_blocks_per_seq]                  int32
+ *   seq_lens        [num_seqs]                                      int32
+ * dtype (PA_DTYPE_F32 or PA_DTYPE_BF16) applies to query, caches and out.
+ * Partials in the V2 workspace are always float32 (layout below).
+ *
+ * Ownership and threading.  Every pointer is caller-owned device memory (except
+ * host-side size outputs).  The library never allocates, frees or synchronises,
+ * and never reads device memory from the host.  It holds no state: calls from
+ * several threads are safe as long as their outputs and workspaces differ.
+ * `out` must not alias any input or the workspace.  All work is enqueued on
+ * `stream` (a hipStream_t; NULL is the default stream) of the current device.
+ *
+ * Errors.  Every check that the host can make is made before anything is
+ * enqueued; on failure nothing is launched and `out` / `workspace` are left
+ * untouched.  PA_ERR_HIP reports a failed launch (hipGetLastError).  PA_OK
+ * means "enqueued".
+ *
+ * Device-side contract (not checkable on the host, enforced defensively):
+ *   - 0 <= seq_lens[s] <= max_seq_len; values outside are clamped into that
+ *     range by the kernels;
+ *   - the first ceil(seq_lens[s] / 16) entries of block_tables[s] are block ids
+ *     in [0, num_blocks); an id outside that range is never dereferenced and
+ *     the 16 tokens it stands for are left out of the softmax;
+ *   - cache slots past the end of a sequence (the tail of its last block) are
+ *     never used: any value there, NaN included, does not reach the output.
+ *
+ * Supported shapes: head_dim 64 or 128; block_size 16; num_q_heads a multiple
+ * of num_kv_heads with group size G <= 16; partition_size a multiple of 16;
+ * num_seqs and num_kv_heads <= 65535.  Anything else returns
+ * PA_ERR_UNSUPPORTED or PA_ERR_INVALID_SHAPE.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+    PA_ERR_INVALID_SHAPE = 2,      /* negative or inconsistent sizes */
+    PA_ERR_UNSUPPORTED = 3,        /* valid, but outside the supported shapes */
+    PA_ERR_WORKSPACE_TOO_SMALL = 4,
+    PA_ERR_HIP = 5,                /* a HIP launch failed */
+    PA_ERR_INVALID_ARGUMENT = 6    /* non-finite or non-positive scale, bad enum */
+} pa_status_t;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *pa_status_string(pa_status_t status);
+
+/*
+ * Bytes of V2 workspace for this problem: three float32 arrays, each starting
+ * on a 256-byte boundary, with P_max = ceil(max_seq_len / partition_size):
+ *   tmp_output  [num_seqs][num_q_heads][P_max][head_dim]   at offset 0
+ *   exp_sums    [num_seqs][num_q_heads][P_max]             at *exp_sums_offset
+ *   max_logits  [num_seqs][num_q_heads][P_max]             at *max_logits_offset
+ * max_logits holds the largest scaled logit of each partition (natural-log
+ * units); exp_sums holds sum_t exp(z_t - max_logit) over the partition;
+ * tmp_output holds the partition's normalised output sum_t exp(z_t - m) v_t / s.
+ * (The pre-allocated intermediates of commit 490ff98, "Three changes", item 2.)
+ * Returns 0 when there is nothing to hold (num_seqs or max_seq_len is 0) or
+ * when the arguments are invalid (negative sizes, partition_size not a
+ * positive multiple of 16).
+ */
+size_t pa_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                         int partition_size);
+
+/* Offsets of the workspace arrays described at pa_workspace_size.  Any output
+ * pointer may be NULL.  Returns PA_ERR_INVALID_SHAPE for invalid sizes. */
+pa_status_t pa_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                                int partition_size, size_t *exp_sums_offset,
+                                size_t *max_logits_offset, int *max_partitions);
+
+/*
+ * V1: single pass.  One workgroup per (sequence, kv head) walks all of the
+ * sequence's blocks with an online-softmax accumulator {running max, running
+ * exp-sum, running output}, merging with the factor exp(old max - new max)
+ * (commit 490ff98, the summary_statistics message; commit 15ef28e, "[OPT]
+ * PagedAttention V2 implementation", the V1 limitation).  Writes out directly.
+ */
+pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
+                         const void *value_cache, const int32_t *block_tables,
+                         const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int max_seq_len, float scale, pa_dtype_t dtype, void *stream);
+
+/*
+ * V2: split-KV.  Phase 1, one workgroup per (partition, kv head, sequence),
+ * writes each partition's partials into the workspace; Phase 2, one workgroup
+ * per (query head, sequence), merges them into out (commit 15ef28e, "[OPT]
+ * PagedAttention V2 implementation", Phase 1 and Phase 2).  Two launches on
+ * `stream`, no host synchronisation.  workspace_bytes must be at least
+ * pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+ * partition_size); the workspace may be reused by later calls on the same
+ * stream.  A sequence with L == 0 gets an all-zero output row.
+ */
+pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
+                         const void *value_cache, const int32_t *block_tables,
+                         const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int max_seq_len, float scale, pa_dtype_t dtype, int partition_size,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
+ * for partitions p < ceil(L / partition_size) of each sequence; other entries
+ * are not written.  Same arguments as pa_decode_v2, without out. */
+pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, int max_seq_len, float scale,
+                                  pa_dtype_t dtype, int partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* V2 Phase 2 alone: merges the workspace partials into out with the
+ * log-sum-exp rescale (commit 15ef28e, "[OPT] PagedAttention V2
+ * implementation", Phase 2).  Reads only partitions p < ceil(L / partition_size)
+ * of each sequence. */
+pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int head_dim, int max_seq_len, pa_dtype_t dtype,
+                                int partition_size, const void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * Dispatch rule between V1 and V2: returns 1 (use V2) iff max_seq_len > 8192,
+ * the threshold of commit 900ae0b ("THE SINGLE HIGHEST-IMPACT CODE CHANGE")
+ * and commit 490ff98 ("Three changes", item 1); 0 otherwise.  The other
+ * arguments are accepted for future occupancy-aware rules and are not used.
+ */
+int pa_select_v2(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size);
+
+/* pa_decode_v1 or pa_decode_v2, chosen by pa_select_v2.  The workspace is only
+ * required (and only checked) when V2 is chosen. */
+pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                      pa_dtype_t dtype, int partition_size, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,218 @@
+"""Python binding of libpa_decode.so (include/pa_decode.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and streams.  There is
+no fallback: if the library is missing or the tensors are not on a GPU, the
+call raises.
+
+Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
+pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
+pa_workspace_layout, pa_select_v2, pa_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
+BLOCK_SIZE = 16
+
+PA_OK = 0
+_DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {pa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library():
+    """Open libpa_decode.so (built by split_kv_paged_pa_amd/build.py); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python split_kv_paged_pa_amd/build.py` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    common = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I]
+    lib.pa_status_string.argtypes = [I]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_workspace_size.argtypes = [I, I, I, I, I]
+    lib.pa_workspace_size.restype = Z
+    lib.pa_workspace_layout.argtypes = [I, I, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z),
+                                        ctypes.POINTER(I)]
+    lib.pa_workspace_layout.restype = I
+    lib.pa_select_v2.argtypes = [I, I, I, I]
+    lib.pa_select_v2.restype = I
+    lib.pa_decode_v1.argtypes = [P] + common + [P]
+    lib.pa_decode_v1.restype = I
+    lib.pa_decode_v2.argtypes = [P] + common + [I, P, Z, P]
+    lib.pa_decode_v2.restype = I
+    lib.pa_decode.argtypes = [P] + common + [I, P, Z, P]
+    lib.pa_decode.restype = I
+    lib.pa_decode_v2_partials.argtypes = common + [I, P, Z, P]
+    lib.pa_decode_v2_partials.restype = I
+    lib.pa_decode_v2_reduce.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
+    lib.pa_decode_v2_reduce.restype = I
+    _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def pa_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                      partition_size: int) -> int:
+    return int(load_library().pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                                partition_size))
+
+
+def pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size):
+    """(exp_sums_offset, max_logits_offset, max_partitions) in bytes / count."""
+    e, m, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int()
+    st = load_library().pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                            partition_size, ctypes.byref(e), ctypes.byref(m),
+                                            ctypes.byref(n))
+    if st != PA_OK:
+        raise PagedAttentionError(st, "pa_workspace_layout")
+    return int(e.value), int(m.value), int(n.value)
+
+
+def pa_select_v2(max_seq_len: int, num_seqs: int, num_kv_heads: int, partition_size: int) -> bool:
+    return bool(load_library().pa_select_v2(max_seq_len, num_seqs, num_kv_heads, partition_size))
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(name, t, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len):
+    if query.dtype not in _DTYPE_CODE:
+        raise TypeError(f"query dtype must be float32 or bfloat16, got {query.dtype}")
+    S, Hq, D = query.shape
+    nb, Hkv, B, D2 = key_cache.shape
+    if value_cache.shape != key_cache.shape or D2 != D:
+        raise ValueError("key_cache / value_cache / query shapes disagree")
+    if block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_tables and seq_lens need one row per sequence")
+    args = [_dev("query", query, None, 3),
+            _dev("key_cache", key_cache, query.dtype, 4),
+            _dev("value_cache", value_cache, query.dtype, 4),
+            _dev("block_tables", block_tables, torch.int32, 2),
+            _dev("seq_lens", seq_lens, torch.int32, 1),
+            S, Hq, Hkv, D, B, nb, block_tables.shape[1], int(max_seq_len), float(scale),
+            _DTYPE_CODE[query.dtype]]
+    return args
+
+
+def _check(st, where):
+    if st != PA_OK:
+        raise PagedAttentionError(st, where)
+
+
+def _workspace(ws):
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    _dev("workspace", ws)
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def pa_decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                 stream=None):
+    """V1 single-pass decode into out [S, Hq, D] (same dtype as query)."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    _check(load_library().pa_decode_v1(o, *args, _stream(stream)), "pa_decode_v1")
+
+
+def pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                 partition_size, workspace, stream=None):
+    """V2 split-KV decode: Phase 1 partials into workspace, Phase 2 merge into out."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2(o, *args, int(partition_size), wp, wb, _stream(stream)),
+           "pa_decode_v2")
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+              partition_size, workspace, stream=None):
+    """V1 or V2 as pa_select_v2 decides."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode(o, *args, int(partition_size), wp, wb, _stream(stream)),
+           "pa_decode")
+
+
+def pa_decode_v2_partials(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                          max_seq_len, partition_size, workspace, stream=None):
+    """V2 Phase 1 only: partials into workspace (see workspace_views)."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2_partials(*args, int(partition_size), wp, wb,
+                                                _stream(stream)), "pa_decode_v2_partials")
+
+
+def pa_decode_v2_reduce(out, seq_lens, max_seq_len, partition_size, workspace, stream=None):
+    """V2 Phase 2 only: merge the workspace partials into out [S, Hq, D]."""
+    S, Hq, D = out.shape
+    o = _dev("out", out)
+    if out.dtype not in _DTYPE_CODE:
+        raise TypeError("out must be float32 or bfloat16")
+    sl = _dev("seq_lens", seq_lens, torch.int32, 1)
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2_reduce(o, sl, S, Hq, D, int(max_seq_len),
+                                              _DTYPE_CODE[out.dtype], int(partition_size), wp, wb,
+                                              _stream(stream)), "pa_decode_v2_reduce")
+
+
+def new_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, device="cuda"):
+    """A uint8 device tensor of pa_workspace_size bytes (at least 1 byte)."""
+    n = pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def workspace_views(workspace, num_seqs, num_q_heads, head_dim, max_seq_len, partition_size):
+    """(tmp_out [S,Hq,Pmax,D], exp_sums [S,Hq,Pmax], max_logits [S,Hq,Pmax]) float32 views."""
+    e_off, m_off, n = pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                          partition_size)
+    rows = num_seqs * num_q_heads * n
+    f = workspace.view(torch.uint8)
+    tmp = f[:rows * head_dim * 4].view(torch.float32).view(num_seqs, num_q_heads, n, head_dim)
+    es = f[e_off:e_off + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, n)
+    ml = f[m_off:m_off + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, n)
+    return tmp, es, ml

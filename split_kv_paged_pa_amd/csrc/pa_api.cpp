@@ -1,0 +1,265 @@
+// pa_api.cpp -- the C ABI of libpa_decode.so (declared in include/pa_decode.h):
+// host-side argument checks, workspace carving, V1/V2 dispatch, launches.
+// Every check happens before anything is enqueued; nothing here allocates,
+// synchronises or reads device memory.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pa_decode.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kBlockTokens = 16;
+constexpr int kMaxGroup = 16;
+constexpr int kMaxGridYZ = 65535;
+// V2 is used above this many tokens: the threshold of commit 900ae0b
+// ("THE SINGLE HIGHEST-IMPACT CODE CHANGE") and commit 490ff98 ("Three changes").
+constexpr int kV2MinSeqLen = 8192;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+    int max_parts;
+    size_t exp_off, max_off, total;
+};
+
+// Workspace layout; false if the sizes are invalid.
+bool layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, int partition_size,
+            Layout *out) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return false;
+    if (partition_size < kBlockTokens || partition_size % kBlockTokens != 0) return false;
+    const long long parts = max_seq_len > 0
+                                ? ((long long)max_seq_len + partition_size - 1) / partition_size
+                                : 0;
+    const unsigned long long rows = (unsigned long long)num_seqs * num_q_heads * parts;
+    const unsigned long long tmp = rows * head_dim * sizeof(float);
+    const unsigned long long vec = rows * sizeof(float);
+    if (rows && (tmp / rows / sizeof(float) != (unsigned long long)head_dim)) return false;
+    out->max_parts = (int)parts;
+    out->exp_off = align_up(tmp);
+    out->max_off = out->exp_off + align_up(vec);
+    out->total = rows ? out->max_off + align_up(vec) : 0;
+    return true;
+}
+
+pa_status_t check_problem(const void *query, const void *key_cache, const void *value_cache,
+                          const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                          pa_dtype_t dtype) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seq_len < 0)
+        return PA_ERR_INVALID_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_SHAPE;
+    if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
+        return PA_ERR_INVALID_SHAPE;
+    if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !seq_lens)
+        return PA_ERR_NULL_POINTER;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PA_ERR_INVALID_ARGUMENT;
+    return PA_OK;
+}
+
+pa::Problem make_problem(const void *query, const void *key_cache, const void *value_cache,
+                         const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                         int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                         int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype) {
+    pa::Problem pb;
+    pb.query = query;
+    pb.key_cache = key_cache;
+    pb.value_cache = value_cache;
+    pb.block_tables = block_tables;
+    pb.seq_lens = seq_lens;
+    pb.num_seqs = num_seqs;
+    pb.num_q_heads = num_q_heads;
+    pb.num_kv_heads = num_kv_heads;
+    pb.head_dim = head_dim;
+    pb.num_blocks = num_blocks;
+    pb.max_blocks = max_blocks_per_seq;
+    pb.max_seq_len = max_seq_len;
+    pb.scale = scale;
+    pb.dtype = dtype == PA_DTYPE_BF16 ? pa::Dtype::BF16 : pa::Dtype::F32;
+    return pb;
+}
+
+// Checks the V2 workspace and carves it; *empty is set when nothing needs launching.
+pa_status_t carve(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, int partition_size,
+                  void *workspace, size_t workspace_bytes, pa::Partials *parts) {
+    if (partition_size < kBlockTokens || partition_size % kBlockTokens != 0)
+        return PA_ERR_UNSUPPORTED;
+    if ((long long)max_seq_len + partition_size > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    Layout lay;
+    if (!layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &lay))
+        return PA_ERR_INVALID_SHAPE;
+    if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (lay.total > 0 && !workspace) return PA_ERR_NULL_POINTER;
+    if (lay.total > 0 && !aligned16(workspace)) return PA_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(workspace);
+    parts->tmp_out = reinterpret_cast<float *>(base);
+    parts->exp_sums = reinterpret_cast<float *>(base + lay.exp_off);
+    parts->max_logits = reinterpret_cast<float *>(base + lay.max_off);
+    parts->partition_size = partition_size;
+    parts->max_parts = lay.max_parts;
+    return PA_OK;
+}
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(pa_status_t status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL_POINTER: return "PA_ERR_NULL_POINTER: a required pointer is NULL";
+        case PA_ERR_INVALID_SHAPE: return "PA_ERR_INVALID_SHAPE: negative or inconsistent sizes";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape outside the supported set";
+        case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+        case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed";
+        case PA_ERR_INVALID_ARGUMENT:
+            return "PA_ERR_INVALID_ARGUMENT: bad dtype, non-finite scale or misaligned pointer";
+    }
+    return "unknown pa_status_t";
+}
+
+size_t pa_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                         int partition_size) {
+    Layout lay;
+    if (!layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &lay)) return 0;
+    return lay.total;
+}
+
+pa_status_t pa_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                                int partition_size, size_t *exp_sums_offset,
+                                size_t *max_logits_offset, int *max_partitions) {
+    Layout lay;
+    if (!layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &lay))
+        return PA_ERR_INVALID_SHAPE;
+    if (exp_sums_offset) *exp_sums_offset = lay.exp_off;
+    if (max_logits_offset) *max_logits_offset = lay.max_off;
+    if (max_partitions) *max_partitions = lay.max_parts;
+    return PA_OK;
+}
+
+int pa_select_v2(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {
+    (void)num_seqs;
+    (void)num_kv_heads;
+    (void)partition_size;
+    return max_seq_len > kV2MinSeqLen ? 1 : 0;
+}
+
+pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
+                         const void *value_cache, const int32_t *block_tables,
+                         const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int max_seq_len, float scale, pa_dtype_t dtype, void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!out) return PA_ERR_NULL_POINTER;
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    return from_hip(pa::launch_single_pass(pb, out, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, int max_seq_len, float scale,
+                                  pa_dtype_t dtype, int partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    pa::Partials parts;
+    st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, workspace,
+               workspace_bytes, &parts);
+    if (st != PA_OK || num_seqs == 0 || parts.max_parts == 0) return st;
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    return from_hip(pa::launch_partitions(pb, parts, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int head_dim, int max_seq_len, pa_dtype_t dtype,
+                                int partition_size, const void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+        return PA_ERR_INVALID_SHAPE;
+    if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARGUMENT;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+    pa::Partials parts;
+    pa_status_t st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size,
+                           const_cast<void *>(workspace), workspace_bytes, &parts);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!out || !seq_lens) return PA_ERR_NULL_POINTER;
+    return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
+                                      dtype == PA_DTYPE_BF16 ? pa::Dtype::BF16 : pa::Dtype::F32,
+                                      parts, out, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
+                         const void *value_cache, const int32_t *block_tables,
+                         const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int max_seq_len, float scale, pa_dtype_t dtype, int partition_size,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    pa::Partials parts;
+    st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, workspace,
+               workspace_bytes, &parts);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!out) return PA_ERR_NULL_POINTER;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (parts.max_parts > 0) {
+        st = from_hip(pa::launch_partitions(pb, parts, hs));
+        if (st != PA_OK) return st;
+    }
+    return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
+                                      pb.dtype, parts, out, hs));
+}
+
+pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                      pa_dtype_t dtype, int partition_size, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (pa_select_v2(max_seq_len, num_seqs, num_kv_heads, partition_size)) {
+        return pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                            num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                            max_blocks_per_seq, max_seq_len, scale, dtype, partition_size,
+                            workspace, workspace_bytes, stream);
+    }
+    return pa_decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_seq_len, scale, dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,497 @@
+// pa_kernels.hip -- gfx950 (CDNA4) kernels for paged single-query decode attention.
+//
+// Method (project_6 commit pages):
+//   - commit 15ef28e (paged_attention_v2_pytorch.py), "[OPT] PagedAttention V2
+//     implementation": Phase 1 computes, per (sequence, head, partition), the
+//     logits, their softmax statistics and the value-weighted sum, and stores
+//     the partition output, exp-sum and max logit; Phase 2 takes the global max
+//     over partitions, rescales each partition by exp(m_p - M) * s_p and sums
+//     the partition outputs with those weights over their total.  V1 walks the
+//     whole sequence in one unit of work.
+//   - commit 490ff98 (paged_attn.py), the summary_statistics message: the
+//     running state {max, exp-sum, output} of online softmax and its merge
+//     with the factor exp(old max - new max); kv heads are independent and the
+//     query heads of one group are processed together.
+//   - commit 15ef28e, "[OPT] Vectorize paged_attention_v2": keys and values are
+//     fetched through the per-sequence block id list, 16 tokens per block, and
+//     each kv head is broadcast over its query-head group.
+//
+// Design for gfx950 (what differs from the pages' PyTorch design):
+//   - One workgroup of NW wave64s per (partition, kv head, sequence).  All G
+//     query heads of the group sit in the N dimension of one 16x16 MFMA tile,
+//     so every key/value block is read from HBM once for the whole group.
+//   - A wave owns whole 16-token blocks (blocks j = first + w, first + w + NW, ...).
+//     Lane l loads 16 bytes of token (l % 16), at byte 64*c + 16*(l / 16) of the
+//     row, for c = 0 .. NC-1: four dwordx4 loads per lane cover a 4 KiB bf16
+//     D=128 block, every 64-byte segment fully used.
+//   - QK^T: MFMA with A = keys (rows = tokens), B = Q^T (cols = heads).  The
+//     result tile holds, in lane (g, grp) register i, the logit of token
+//     4*grp + i for head g -- exactly the B-operand layout P^T needs for PV,
+//     so the softmax weights never leave their lane.
+//   - V is read row-major (tokens x d), but PV reduces over tokens, which MFMA
+//     wants contiguous per lane.  The transpose is done in registers by one
+//     MFMA against a 0/1 selection matrix (exact: each output is one value
+//     times 1 plus zeros); the result is the A operand of O^T = V^T P^T.
+//     No LDS traffic in the block loop.
+//   - Masked tokens (past the sequence end) get logit -inf and their value
+//     registers are zeroed before any MFMA touches them, so stale or NaN cache
+//     slots cannot leak through 0 * NaN.
+//   - Exponentials: exp(x) = 2^(x log2 e) on v_exp_f32.
+//   - Waves merge their {max, exp-sum, output} states once, through LDS, in a
+//     fixed order: results are bitwise reproducible run to run (no atomics).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlockTokens = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ s16x4 pack_bf16_rne(float a, float b, float c, float d) {
+    u32x2 w = {bf16_rne(a) | (bf16_rne(b) << 16), bf16_rne(c) | (bf16_rne(d) << 16)};
+    return __builtin_bit_cast(s16x4, w);
+}
+
+// Values that are already bf16 numbers held in float32: keep the top half.
+__device__ __forceinline__ s16x4 pack_bf16_exact(f32x4 v) {
+    u32x2 w = {(__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u),
+               (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u)};
+    return __builtin_bit_cast(s16x4, w);
+}
+
+__device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.x, v.y}); }
+__device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
+
+// ---------------------------------------------------------------------------
+// Element-type specific MFMA steps.  For both types a lane works on "chunk c":
+// the 16 bytes at byte 64*c + 16*grp of a row (grp = lane / 16), i.e. E
+// consecutive d values starting at d = c*4E + grp*E.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+// bf16 storage (uint16 bit patterns): v_mfma_f32_16x16x16_bf16, 4 values per lane.
+template <> struct Mma<uint16_t> {
+    static constexpr int E = 8;        // elements per 16-byte chunk
+    static constexpr int kTiles = 2;   // f32x4 accumulator tiles per chunk
+
+    // S[t][g] += sum over the chunk's d of K[t][d] Q[g][d].
+    static __device__ __forceinline__ void qk(f32x4 &s, uint4 k, uint4 q) {
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo_half(k), lo_half(q), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi_half(k), hi_half(q), s, 0, 0, 0);
+    }
+
+    struct Consts { s16x4 ident; };
+    static __device__ __forceinline__ Consts consts(int l16, int grp) {
+        float e[4];
+        for (int i = 0; i < 4; ++i) e[i] = (4 * grp + i == l16) ? 1.f : 0.f;
+        return {pack_bf16_rne(e[0], e[1], e[2], e[3])};
+    }
+
+    struct Probs { s16x4 p; };
+    static __device__ __forceinline__ Probs probs(const float *p) {
+        return {pack_bf16_rne(p[0], p[1], p[2], p[3])};
+    }
+
+    // acc[h] (lane (g, grp), register r) += sum_t P[g][t] V[t][c*32 + grp*8 + 4h + r].
+    static __device__ __forceinline__ void pv(f32x4 *acc, uint4 v, const Consts &k, const Probs &pr) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        // Transpose: T[t][j] = V[t][d(j)], lane (j, grp) register r = token 4*grp + r.
+        f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo_half(v), k.ident, zero, 0, 0, 0);
+        f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi_half(v), k.ident, zero, 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16_exact(t0), pr.p, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16_exact(t1), pr.p, acc[1], 0, 0, 0);
+    }
+
+    static __device__ __forceinline__ float to_float(uint16_t x) {
+        return __uint_as_float((uint32_t)x << 16);
+    }
+    static __device__ __forceinline__ uint16_t from_float(float x) { return (uint16_t)bf16_rne(x); }
+};
+
+// float32 storage: v_mfma_f32_16x16x4_f32, one value per lane per MFMA.
+template <> struct Mma<float> {
+    static constexpr int E = 4;
+    static constexpr int kTiles = 1;
+
+    static __device__ __forceinline__ void qk(f32x4 &s, uint4 k, uint4 q) {
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), __uint_as_float(q.y), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), __uint_as_float(q.z), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), __uint_as_float(q.w), s, 0, 0, 0);
+    }
+
+    // sel[e] in lane (j, grp) is 1 iff j == 4*grp + e.
+    struct Consts { float sel[4]; };
+    static __device__ __forceinline__ Consts consts(int l16, int grp) {
+        Consts c;
+        for (int e = 0; e < 4; ++e) c.sel[e] = (l16 == 4 * grp + e) ? 1.f : 0.f;
+        return c;
+    }
+
+    struct Probs { float p[4]; };
+    static __device__ __forceinline__ Probs probs(const float *p) { return {{p[0], p[1], p[2], p[3]}}; }
+
+    // acc[0] (lane (g, grp), register r) += sum_t P[g][t] V[t][c*16 + grp*4 + r].
+    static __device__ __forceinline__ void pv(f32x4 *acc, uint4 v, const Consts &k, const Probs &pr) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        // Transpose: T[t][j] = V[t][c*16 + j]; lane (j, grp) register r = token 4*grp + r.
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), k.sel[0], t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), k.sel[1], t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), k.sel[2], t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), k.sel[3], t, 0, 0, 0);
+        // Token 4*k + r of the block is the MFMA-r reduction index k.
+        for (int r = 0; r < 4; ++r)
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(t[r], pr.p[r], acc[0], 0, 0, 0);
+    }
+
+    static __device__ __forceinline__ float to_float(float x) { return x; }
+    static __device__ __forceinline__ float from_float(float x) { return x; }
+};
+
+// ---------------------------------------------------------------------------
+// Phase 1 (kFinal = false): one workgroup per (partition p, kv head, sequence)
+// writes that partition's partials.  V1 (kFinal = true): one workgroup per
+// (kv head, sequence) covers the whole sequence and writes the output.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, bool kFinal>
+__global__ __launch_bounds__(NW * 64) void attend_kernel(
+    const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
+    int num_kv_heads, int group, int num_blocks, int max_blocks, int max_seq_len, float scale,
+    int partition_size, int max_parts, float *__restrict__ tmp_out, float *__restrict__ exp_sums,
+    float *__restrict__ max_logits, T *__restrict__ out) {
+    using M = Mma<T>;
+    constexpr int E = M::E;
+    constexpr int NC = D / (4 * E);          // 16-byte chunks per lane per row
+    constexpr int ROW16 = D / E;             // 16-byte units per row
+    constexpr int NT = NC * M::kTiles;       // accumulator tiles per lane
+    constexpr int LDS_STRIDE = D + 4;
+
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
+    __shared__ float sm_f[NW][16];
+    __shared__ float sm_o[NW][16][LDS_STRIDE];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    int t_begin = 0, t_end = L;
+    if (!kFinal) {
+        t_begin = p * partition_size;
+        if (t_begin >= L) return;  // uniform over the workgroup
+        t_end = min(t_begin + partition_size, L);
+    }
+    const int j_begin = t_begin / kBlockTokens;
+    const int j_end = (t_end + kBlockTokens - 1) / kBlockTokens;
+
+    // Q^T operand: lane (g, grp) holds chunk c of query head kvh*G + g (zero for g >= G).
+    const int g = l16;
+    uint4 qv[NC];
+    if (g < group) {
+        const uint4 *qrow = reinterpret_cast<const uint4 *>(
+            query + ((size_t)s * num_q_heads + (size_t)kvh * group + g) * D);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = qrow[c * 4 + grp];
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = make_uint4(0, 0, 0, 0);
+    }
+    const typename M::Consts kc = M::consts(l16, grp);
+
+    float m_run = -INFINITY;  // running max logit of column g
+    float l_run = 0.f;        // this lane's share of the running exp-sum
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int32_t *bt = block_tables + (size_t)s * max_blocks;
+    const size_t slab = (size_t)kBlockTokens * D;  // elements of one (block, kv head) slab
+
+    for (int j = j_begin + w; j < j_end; j += NW) {
+        const int phys = __builtin_amdgcn_readfirstlane(bt[j]);
+        if ((unsigned)phys >= (unsigned)num_blocks) continue;  // out-of-contract id: skip block
+        const uint4 *kp = reinterpret_cast<const uint4 *>(
+                              key_cache + ((size_t)phys * num_kv_heads + kvh) * slab) +
+                          l16 * ROW16 + grp;
+        const uint4 *vp = reinterpret_cast<const uint4 *>(
+                              value_cache + ((size_t)phys * num_kv_heads + kvh) * slab) +
+                          l16 * ROW16 + grp;
+        uint4 kr[NC], vr[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kr[c] = kp[c * 4];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vr[c] = vp[c * 4];
+
+        const int valid = t_end - j * kBlockTokens;  // tokens of this block in range (>= 1)
+
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) M::qk(sacc, kr[c], qv[c]);
+
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * scale : -INFINITY;
+        float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = exp_e(m_run - m_new);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = exp_e(z[i] - m_new);
+        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+
+        if (l16 >= valid) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) vr[c] = make_uint4(0, 0, 0, 0);
+        }
+        const typename M::Probs pb = M::probs(pr);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) M::pv(&acc[c * M::kTiles], vr[c], kc, pb);
+    }
+
+    // Full exp-sum of column g over the wave.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // Publish the wave's state: lane (g, grp) owns d = c*4E + grp*E + [0, E).
+    if (grp == 0) {
+        sm_m[w][g] = m_run;
+        sm_l[w][g] = l_run;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int t = 0; t < M::kTiles; ++t) {
+            float *dst = &sm_o[w][g][c * 4 * E + grp * E + t * 4];
+            *reinterpret_cast<f32x4 *>(dst) = acc[c * M::kTiles + t];
+        }
+    }
+    __syncthreads();
+
+    // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
+    if (threadIdx.x < 16) {
+        const int gg = threadIdx.x;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[ww][gg]);
+        float f[NW];
+        float total = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[ww][gg] - mx);
+            total += f[ww] * sm_l[ww][gg];
+        }
+        const float inv = total > 0.f ? 1.f / total : 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
+        if (!kFinal && gg < group) {
+            const size_t row = ((size_t)s * num_q_heads + (size_t)kvh * group + gg) * max_parts + p;
+            exp_sums[row] = total;
+            max_logits[row] = mx;
+        }
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < group * D; idx += NW * 64) {
+        const int gg = idx / D;
+        const int d = idx - gg * D;
+        float o = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) o += sm_f[ww][gg] * sm_o[ww][gg][d];
+        const size_t h = (size_t)s * num_q_heads + (size_t)kvh * group + gg;
+        if (kFinal) {
+            out[h * D + d] = M::from_float(o);
+        } else {
+            tmp_out[(h * max_parts + p) * D + d] = o;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2: one workgroup (4 waves) per (query head, sequence).  Each wave takes
+// partitions p = w, w + 4, ...; lane l holds d = l*DPL .. l*DPL + DPL - 1.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reduce_kernel(
+    const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
+    const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
+    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    using M = Mma<T>;
+    constexpr int NW = 4;
+    constexpr int DPL = D / 64;
+    constexpr int CH = 1024;  // partitions staged per round
+    __shared__ float sm_red[NW];
+    __shared__ float sm_w[CH];
+    __shared__ float sm_acc[NW][D];
+    __shared__ float sm_wsum[NW];
+
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const size_t head = (size_t)s * num_q_heads + h;
+    T *orow = out + head * D;
+
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    if (parts == 0) {
+        for (int d = tid; d < D; d += 256) orow[d] = M::from_float(0.f);
+        return;
+    }
+    const float *ml = max_logits + head * max_parts;
+    const float *es = exp_sums + head * max_parts;
+    const float *po = tmp_out + head * max_parts * D;
+
+    float mx = -INFINITY;
+    for (int i = tid; i < parts; i += 256) mx = fmaxf(mx, ml[i]);
+    mx = wave_max(mx);
+    if (lane == 0) sm_red[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+    if (mx == -INFINITY) {  // only reachable when no block id of the sequence was valid
+        for (int d = tid; d < D; d += 256) orow[d] = M::from_float(0.f);
+        return;
+    }
+
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    float wsum = 0.f;
+    for (int p0 = 0; p0 < parts; p0 += CH) {
+        const int n = min(CH, parts - p0);
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) sm_w[i] = exp_e(ml[p0 + i] - mx) * es[p0 + i];
+        __syncthreads();
+        int i = w;
+        for (; i + 3 * NW < n; i += 4 * NW) {
+            float wt[4];
+            float vals[4][DPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wt[u] = sm_w[i + u * NW];
+                const float *src = po + (size_t)(p0 + i + u * NW) * D + lane * DPL;
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) vals[u][k] = src[k];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wsum += wt[u];
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) acc[k] += wt[u] * vals[u][k];
+            }
+        }
+        for (; i < n; i += NW) {
+            const float wt = sm_w[i];
+            const float *src = po + (size_t)(p0 + i) * D + lane * DPL;
+            wsum += wt;
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) acc[k] += wt * src[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) sm_acc[w][lane * DPL + k] = acc[k];
+    if (lane == 0) sm_wsum[w] = wsum;
+    __syncthreads();
+    const float total = (sm_wsum[0] + sm_wsum[1]) + (sm_wsum[2] + sm_wsum[3]);
+    const float inv = 1.f / total;
+    for (int d = tid; d < D; d += 256) {
+        const float o = (sm_acc[0][d] + sm_acc[1][d]) + (sm_acc[2][d] + sm_acc[3][d]);
+        orow[d] = M::from_float(o * inv);
+    }
+}
+
+constexpr int kWaves = 4;
+
+template <typename T, int D, bool kFinal>
+hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
+    const int group = pb.num_q_heads / pb.num_kv_heads;
+    dim3 grid(kFinal ? 1 : parts->max_parts, pb.num_kv_heads, pb.num_seqs);
+    attend_kernel<T, D, kWaves, kFinal><<<grid, kWaves * 64, 0, stream>>>(
+        static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
+        static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
+        pb.num_kv_heads, group, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
+        kFinal ? 0 : parts->partition_size, kFinal ? 0 : parts->max_parts,
+        kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
+        kFinal ? nullptr : parts->max_logits, static_cast<T *>(out));
+    return hipGetLastError();
+}
+
+template <bool kFinal>
+hipError_t dispatch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
+    if (pb.dtype == Dtype::BF16) {
+        return pb.head_dim == 64 ? launch_attend<uint16_t, 64, kFinal>(pb, parts, out, stream)
+                                 : launch_attend<uint16_t, 128, kFinal>(pb, parts, out, stream);
+    }
+    return pb.head_dim == 64 ? launch_attend<float, 64, kFinal>(pb, parts, out, stream)
+                             : launch_attend<float, 128, kFinal>(pb, parts, out, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_heads, int max_seq_len,
+                           const Partials &parts, void *out, hipStream_t stream) {
+    dim3 grid(num_q_heads, num_seqs);
+    reduce_kernel<T, D><<<grid, 256, 0, stream>>>(parts.tmp_out, parts.exp_sums, parts.max_logits,
+                                                  seq_lens, num_q_heads, max_seq_len,
+                                                  parts.partition_size, parts.max_parts,
+                                                  static_cast<T *>(out));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream) {
+    return dispatch_attend<true>(pb, nullptr, out, stream);
+}
+
+hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream) {
+    return dispatch_attend<false>(pb, &parts, nullptr, stream);
+}
+
+hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
+                         int max_seq_len, Dtype dtype, const Partials &parts, void *out,
+                         hipStream_t stream) {
+    if (dtype == Dtype::BF16) {
+        return head_dim == 64
+                   ? launch_reduce_t<uint16_t, 64>(seq_lens, num_seqs, num_q_heads, max_seq_len, parts, out, stream)
+                   : launch_reduce_t<uint16_t, 128>(seq_lens, num_seqs, num_q_heads, max_seq_len, parts, out, stream);
+    }
+    return head_dim == 64
+               ? launch_reduce_t<float, 64>(seq_lens, num_seqs, num_q_heads, max_seq_len, parts, out, stream)
+               : launch_reduce_t<float, 128>(seq_lens, num_seqs, num_q_heads, max_seq_len, parts, out, stream);
+}
+
+}  // namespace pa

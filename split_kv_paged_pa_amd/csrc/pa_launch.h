@@ -1,0 +1,44 @@
+// pa_launch.h -- internal interface between the C-ABI layer (pa_api.cpp) and the
+// HIP kernels (pa_kernels.hip).  Not installed, not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class Dtype : int { F32 = 0, BF16 = 1 };
+
+// One decode batch, already validated by the ABI layer.
+struct Problem {
+    const void *query;          // [S][Hq][D]
+    const void *key_cache;      // [num_blocks][Hkv][16][D]
+    const void *value_cache;    // [num_blocks][Hkv][16][D]
+    const int32_t *block_tables;  // [S][max_blocks]
+    const int32_t *seq_lens;    // [S]
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int num_blocks, max_blocks, max_seq_len;
+    float scale;
+    Dtype dtype;
+};
+
+// Float32 partials of the split-KV form, carved out of the caller's workspace.
+struct Partials {
+    float *tmp_out;      // [S][Hq][max_parts][D]
+    float *exp_sums;     // [S][Hq][max_parts]
+    float *max_logits;   // [S][Hq][max_parts]
+    int partition_size;
+    int max_parts;
+};
+
+// V1: one workgroup per (kv head, sequence) over the whole sequence -> out.
+hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream);
+// V2 Phase 1: one workgroup per (partition, kv head, sequence) -> partials.
+hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream);
+// V2 Phase 2: one workgroup per (query head, sequence): partials -> out.
+hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
+                         int max_seq_len, Dtype dtype, const Partials &parts, void *out,
+                         hipStream_t stream);
+
+}  // namespace pa

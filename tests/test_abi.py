@@ -1,0 +1,127 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects every invalid argument before any HIP call is made.
+No call here gets past validation, so nothing touches a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import split_kv_paged_pa_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_decode.h")
+
+OK, NULLP, SHAPE, UNSUP, WS, HIP, ARG = range(7)
+FAKE = 0x10000  # never dereferenced: each case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = pa.load_library()
+    names = declared_functions()
+    assert {"pa_decode_v1", "pa_decode_v2", "pa_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pa_decode.h but not exported"
+
+
+def test_status_strings():
+    for st in range(7):
+        assert pa.pa_status_string(st).startswith("PA_")
+
+
+def test_workspace_size_arithmetic():
+    # 100000 tokens, 32 query heads, D 128: 196 partitions of 512, 98 of 1024.
+    def expect(S, Hq, D, L, P):
+        n = -(-L // P)
+        a = lambda x: -(-x // 256) * 256
+        rows = S * Hq * n
+        return a(rows * D * 4) + 2 * a(rows * 4) if rows else 0
+    assert pa.pa_workspace_size(1, 32, 128, 100000, 512) == expect(1, 32, 128, 100000, 512) == 3261440
+    assert pa.pa_workspace_size(1, 32, 128, 100000, 1024) == 1630720
+    assert pa.pa_workspace_layout(1, 32, 128, 100000, 1024)[2] == 98
+    assert pa.pa_workspace_layout(1, 32, 128, 100000, 512)[2] == 196
+    assert pa.pa_workspace_size(16, 32, 128, 32768, 1024) == expect(16, 32, 128, 32768, 1024)
+    assert pa.pa_workspace_size(0, 32, 128, 1000, 512) == 0
+    assert pa.pa_workspace_size(3, 32, 128, 0, 512) == 0
+    assert pa.pa_workspace_size(1, 32, 128, 1000, 24) == 0      # P not a multiple of 16
+    assert pa.pa_workspace_size(-1, 32, 128, 1000, 512) == 0
+
+
+def test_select_v2_threshold():
+    assert pa.pa_select_v2(8192, 1, 4, 512) is False
+    assert pa.pa_select_v2(8193, 1, 4, 512) is True
+    assert pa.pa_select_v2(100000, 1, 4, 1024) is True
+
+
+def call_v2(lib, **over):
+    a = dict(out=FAKE, query=FAKE, key=FAKE, value=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=8, Hkv=2, D=128,
+             bs=16, nb=100, mb=64, L=1000, scale=0.088, dtype=1, P=512, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(over)
+    return lib.pa_decode_v2(a["out"], a["query"], a["key"], a["value"], a["bt"], a["sl"], a["S"],
+                            a["Hq"], a["Hkv"], a["D"], a["bs"], a["nb"], a["mb"], a["L"],
+                            a["scale"], a["dtype"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+CASES = [
+    ("null query", dict(query=None), NULLP),
+    ("null out", dict(out=None), NULLP),
+    ("null block table", dict(bt=None), NULLP),
+    ("null workspace", dict(ws=None), NULLP),
+    ("heads not grouped", dict(Hq=9), SHAPE),
+    ("negative seqs", dict(S=-1), SHAPE),
+    ("max_seq_len beyond table", dict(L=64 * 16 + 1), SHAPE),
+    ("group of 32", dict(Hq=64), UNSUP),
+    ("head_dim 96", dict(D=96), UNSUP),
+    ("block size 32", dict(bs=32), UNSUP),
+    ("partition 24", dict(P=24), UNSUP),
+    ("partition 0", dict(P=0), UNSUP),
+    ("too many seqs", dict(S=70000), UNSUP),
+    ("workspace too small", dict(wsb=1000), WS),
+    ("nan scale", dict(scale=math.nan), ARG),
+    ("inf scale", dict(scale=math.inf), ARG),
+    ("bad dtype", dict(dtype=7), ARG),
+    ("misaligned key cache", dict(key=FAKE + 2), ARG),
+    ("misaligned workspace", dict(ws=FAKE + 4), ARG),
+]
+
+
+@pytest.mark.parametrize("what,over,status", CASES, ids=[c[0] for c in CASES])
+def test_v2_rejects_before_launch(what, over, status):
+    assert call_v2(pa.load_library(), **over) == status
+
+
+def test_v1_and_dispatch_reject_before_launch():
+    lib = pa.load_library()
+    common = (FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 16, 100, 64, 1000, 0.088, 1)
+    assert lib.pa_decode_v1(None, *common, None) == NULLP
+    bad = (FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 3, 128, 16, 100, 64, 1000, 0.088, 1)
+    assert lib.pa_decode_v1(FAKE, *bad, None) == SHAPE
+    # pa_decode picks V2 above 8192 tokens, which needs the workspace.
+    big = (FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 16, 100, 1024, 9000, 0.088, 1)
+    assert lib.pa_decode(FAKE, *big, 1024, None, 0, None) == WS
+    assert lib.pa_decode_v2_reduce(FAKE, FAKE, 2, 8, 128, 9000, 1, 1024, None, 0, None) == WS
+    assert lib.pa_decode_v2_reduce(FAKE, FAKE, 2, 8, 96, 9000, 1, 1024, FAKE, 1 << 30, None) == UNSUP
+
+
+def test_empty_batch_is_a_no_op():
+    lib = pa.load_library()
+    # num_seqs == 0: valid, nothing to launch, pointers may be NULL.
+    assert call_v2(lib, S=0, out=None, query=None, key=None, value=None, bt=None, sl=None,
+                   ws=None, wsb=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 64)
+    kc = torch.zeros(4, 2, 16, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.pa_decode_v1(torch.zeros_like(q), q, kc, kc, torch.zeros(1, 4, dtype=torch.int32),
+                        torch.ones(1, dtype=torch.int32), 0.125, 1)

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small batches (several blocks, partitions and waves, ragged tails, NaN-poisoned
+unused slots and workspace) are compared on every output; the five named
+workloads at full size are compared on every output where the oracle is quick
+(tiny_f32_2k, long_100k_gqa8, batch16_1k_32k) and on sampled (seq, head) rows
+otherwise.  Phase 1 and Phase 2 are also checked alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_kv_paged_pa_amd as pa
+from parity import DeviceBatch, assert_close, oracle_out, require_gpu, sample_rows, to_f64
+from split_kv_paged_pa_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [1, 15, 16, 17, 511, 512, 513, 1023, 1024, 1025, 3000, 0]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
+
+
+SMALL = [("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 128, 32, 4), ("bf16", 64, 16, 1),
+         ("bf16", 128, 40, 8), ("bf16", 128, 8, 8)]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", SMALL, ids=lambda x: str(x))
+@pytest.mark.parametrize("variant,P", [("v1", None), ("v2", 16), ("v2", 512), ("v2", 1024),
+                                       ("v2", 4096)])
+def test_small_ragged(dtype, D, Hq, Hkv, variant, P):
+    spec = wl.custom("small", 101, dtype, Hq, Hkv, D, EDGE_LENS)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    print(f"[case] small {dtype} D={D} Hq={Hq} Hkv={Hkv} {variant} P={P}", flush=True)
+    out = db.run(variant, P)
+    ref = oracle_out(b)
+    assert_close(to_f64(out), ref, dtype, f"{variant} P={P}")
+
+
+def test_zero_length_rows_are_zero():
+    spec = wl.custom("zeros", 102, "bf16", 8, 2, 128, [0, 40, 0])
+    db = DeviceBatch(wl.generate(spec))
+    for out in (db.run_v1(), db.run_v2(512)):
+        o = to_f64(out)
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        assert np.all(np.isfinite(o[1]))
+
+
+def test_all_empty_batch():
+    spec = wl.custom("empty", 103, "f32", 4, 2, 64, [0, 0], num_blocks=1)
+    db = DeviceBatch(wl.generate(spec))
+    db.max_seq_len = 0
+    o1 = to_f64(db.run_v1())
+    o2 = to_f64(db.run_v2(512))
+    assert np.all(o1 == 0) and np.all(o2 == 0)
+
+
+def test_many_partitions_reduce_chunks():
+    """P = 16 over 20000 tokens: 1250 partitions, more than one staging round of the reduce."""
+    spec = wl.custom("manyparts", 104, "bf16", 16, 1, 128, [20000, 7])
+    b = wl.generate(spec)
+    out = DeviceBatch(b).run_v2(16)
+    assert_close(to_f64(out), oracle_out(b), "bf16", "P=16, 1250 partitions")
+
+
+def test_outlier_keys_stability():
+    spec = wl.custom("outliers", 105, "bf16", 16, 2, 128, [5000, 300, 9000],
+                     outlier_frac=0.02, outlier_mult=40.0)
+    b = wl.generate(spec)
+    ref = oracle_out(b)
+    db = DeviceBatch(b)
+    for variant, P in (("v1", None), ("v2", 512), ("v2", 1024)):
+        assert_close(to_f64(db.run(variant, P)), ref, "bf16", f"outliers {variant} P={P}")
+
+
+def test_deterministic_bitwise():
+    spec = wl.custom("det", 106, "bf16", 32, 4, 128, [7777, 300])
+    db = DeviceBatch(wl.generate(spec))
+    for variant, P in (("v1", None), ("v2", 512)):
+        a = db.run(variant, P)
+        b = db.run(variant, P)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), variant
+
+
+def test_block_relabel_bitwise():
+    """Permuting the pool and rewriting the table gives bit-identical output."""
+    spec = wl.custom("relabel", 107, "bf16", 8, 2, 128, [900, 33, 2048])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    base = [db.run_v1(), db.run_v2(512)]
+    perm = torch.randperm(b.key_cache.shape[0], generator=torch.Generator().manual_seed(0))
+    inv = torch.argsort(perm)
+    bt = b.block_tables.clone()
+    valid = bt >= 0
+    bt[valid] = inv[bt[valid].long()].int()
+    b2 = wl.Batch(spec, b.query, b.key_cache[perm].contiguous(), b.value_cache[perm].contiguous(),
+                  bt, b.seq_lens)
+    db2 = DeviceBatch(b2)
+    moved = [db2.run_v1(), db2.run_v2(512)]
+    for x, y in zip(base, moved):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_out_of_range_block_ids_are_skipped():
+    """Ids outside [0, num_blocks) are never read; their tokens leave the softmax."""
+    spec = wl.custom("badids", 108, "f32", 8, 2, 64, [100, 64])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    bt = b.block_tables.clone()
+    bt[0, 2] = -7
+    bt[1, 0] = b.key_cache.shape[0] + 3
+    db.block_tables = bt.to("cuda")
+    # Reference: the same sequences with those blocks' tokens zero-weighted, i.e. the
+    # oracle over a copy whose removed tokens carry logit -inf: rebuild without them.
+    q, kc, vc, bt_np, _ = b.numpy()
+    keep0 = [j for j in range(7) if j != 2]
+    keep1 = [1, 2, 3]
+    rows = []
+    for s, keep, L in ((0, keep0, 100), (1, keep1, 64)):
+        toks = [t for t in range(L) if (t // 16) in keep]
+        dense_k = np.stack([kc[bt_np[s, t // 16], :, t % 16] for t in toks])
+        dense_v = np.stack([vc[bt_np[s, t // 16], :, t % 16] for t in toks])
+        n = len(toks)
+        nb = -(-n // 16)
+        kk = np.full((nb, 2, 16, 64), np.nan, np.float32)
+        vv = np.full((nb, 2, 16, 64), np.nan, np.float32)
+        for i in range(n):
+            kk[i // 16, :, i % 16] = dense_k[i]
+            vv[i // 16, :, i % 16] = dense_v[i]
+        ref = oracle.decode(np.ascontiguousarray(q[s:s + 1]), kk, vv,
+                            np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
+                            spec.scale, dtype="f32")
+        rows.append(ref[0])
+    ref = np.stack(rows)
+    for out in (db.run_v1(), db.run_v2(32)):
+        assert_close(to_f64(out), ref, "f32", "skipped block ids")
+
+
+def test_phase1_partials_match_oracle():
+    spec = wl.custom("p1", 109, "bf16", 32, 4, 128, [3000, 17, 1024, 0])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    P = 512
+    ws = db.workspace(P)
+    pa.pa_decode_v2_partials(*db.args(), P, ws)
+    tmp, es, ml = (to_f64(x) for x in pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads,
+                                                         spec.head_dim, db.max_seq_len, P))
+    q, kc, vc, bt, sl = b.numpy()
+    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P, dtype="bf16",
+                                     max_partitions=tmp.shape[2])
+    for s, L in enumerate(sl):
+        n = oracle.num_partitions(L, P)
+        assert np.all(np.abs(ml[s, :, :n] - rml[s, :, :n]) <= 1e-5 * (1 + np.abs(rml[s, :, :n])))
+        assert np.all(np.abs(es[s, :, :n] - res[s, :, :n]) <= 1e-2 * res[s, :, :n])
+        assert_close(tmp[s, :, :n], rtmp[s, :, :n], "bf16", f"tmp_output s={s}")
+
+
+def test_phase2_alone_on_oracle_partials():
+    """Phase 2 fed float32-rounded oracle partials vs the oracle merge of the same values."""
+    spec = wl.custom("p2", 110, "f32", 8, 2, 128, [5000, 1, 700, 0])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    P = 256
+    q, kc, vc, bt, sl = b.numpy()
+    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P, dtype="f32")
+    f32 = [np.nan_to_num(x).astype(np.float32) for x in (rtmp, res, rml)]
+    ref = oracle.merge(*(x.astype(np.float64) for x in f32), sl, P)
+    ws = db.workspace(P)
+    tmp, es, ml = pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads, spec.head_dim,
+                                     db.max_seq_len, P)
+    tmp.copy_(torch.from_numpy(f32[0]))
+    es.copy_(torch.from_numpy(f32[1]))
+    ml.copy_(torch.from_numpy(f32[2]))
+    out = torch.full_like(db.query, float("nan"))
+    pa.pa_decode_v2_reduce(out, db.seq_lens, db.max_seq_len, P, ws)
+    g = to_f64(out)
+    err = np.abs(g - ref)
+    assert np.all(err <= 1e-6 * np.maximum(np.abs(ref), 1e-3)), float(err.max())
+
+
+def test_dispatch_threshold():
+    """pa_decode follows the 8192 rule: V1 (no workspace needed) at 8192, V2 above."""
+    assert not pa.pa_select_v2(8192, 1, 4, 1024) and pa.pa_select_v2(8193, 1, 4, 1024)
+    for L in (8192, 8193):
+        spec = wl.custom("dispatch", 111, "bf16", 8, 2, 128, [L])
+        b = wl.generate(spec)
+        db = DeviceBatch(b)
+        out = db.new_out()
+        if L == 8192:
+            pa.pa_decode(out, *db.args(), 1024, None)
+        else:
+            with pytest.raises(pa.PagedAttentionError):
+                pa.pa_decode(out, *db.args(), 1024, None)
+            pa.pa_decode(out, *db.args(), 1024, db.workspace(1024))
+        assert_close(to_f64(out), oracle_out(b), "bf16", f"pa_decode L={L}")
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads at full size.
+# ---------------------------------------------------------------------------
+FULL = [("tiny_f32_2k", None), ("long_100k_gqa8", None), ("batch16_1k_32k", None),
+        ("batch64_mixed_outliers", 160), ("batch8_131k_gqa5", 64)]
+
+
+@pytest.mark.parametrize("name,nrows", FULL, ids=[f[0] for f in FULL])
+def test_named_workload(name, nrows):
+    spec = wl.config(name)
+    print(f"[case] {name}: generating", flush=True)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    rows = None if nrows is None else sample_rows(spec, nrows)
+    print(f"[case] {name}: oracle on {'all' if rows is None else len(rows)} rows", flush=True)
+    ref = oracle_out(b, rows)
+    variants = [("v2", P) for P in spec.partition_sizes] + [("v1", None)]
+    for variant, P in variants:
+        print(f"[case] {name}: {variant} P={P}", flush=True)
+        out = to_f64(db.run(variant, P))
+        got = out if rows is None else out[rows[:, 0], rows[:, 1]]
+        err = assert_close(got, ref, spec.dtype, f"{name} {variant} P={P}")
+        print(f"[case] {name}: {variant} P={P} max abs err {err:.3e}", flush=True)
+        if rows is not None:
+            assert np.all(np.isfinite(out)), "non-finite output outside the sampled rows"
+    del db
+    torch.cuda.empty_cache()
