@@ -1,0 +1,264 @@
+"""Decode-attention benchmark: one long sequence, 100000 tokens, GQA 8.
+
+A step is one full pass of the hot path over one decode batch: V2 Phase 1
+(per-partition attention into the workspace) plus Phase 2 (log-sum-exp merge
+into the output), launched through the C ABI on torch's current stream.
+
+    python bench.py [--steps K] [--warmup W] [--partition-size P] [--variant v2|v1]
+
+Workload long_100k_gqa8: 1 sequence x 100000 tokens, 32 query / 4 kv heads,
+head_dim 128, bf16, 16-token blocks scattered over an 8192-block pool.  The
+204.8 MB of keys and values would fit in MI355X's 256 MB Infinity Cache, so
+the cache pool is replicated `--copies` times and step i reads copy i mod
+copies: every step streams its keys and values from HBM.  Inputs are resident
+in HBM before the timed region starts.
+
+Prints one JSON line with the throughput (KV GB/s), the roofline of the
+dominant kernel (Phase 1) timed with HIP events on the launch stream, the HBM
+traffic measured by rocprofv3 counters when those were taken on the current
+kernel source (else null), and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import split_kv_paged_pa_amd as pa  # noqa: E402
+from split_kv_paged_pa_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV GB/s read and % of HBM peak; decode-attn µs/step at 100K ctx, GQA 8"
+KERNEL_SRC = os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", "pa_kernels.hip")
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def phase1_bytes(spec, P):
+    """Algorithmic bytes of one Phase-1 launch: each K/V row of the actual tokens
+    read once (Hkv*D*es*2 per token), the query, the block-table entries used,
+    seq_lens, and the partials written (D+2 floats per (seq, head, partition))."""
+    es = spec.elem_size
+    lens = spec.seq_lens.astype(np.int64)
+    parts = int(np.sum(-(-lens // P)))
+    kv = int(lens.sum()) * spec.num_kv_heads * spec.head_dim * es * 2
+    q = spec.num_seqs * spec.num_q_heads * spec.head_dim * es
+    tables = int(np.sum(-(-lens // 16))) * 4 + spec.num_seqs * 4
+    partials = parts * spec.num_q_heads * (spec.head_dim + 2) * 4
+    return kv + q + tables + partials, kv
+
+
+def load_traffic(workload, P):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{P}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t
+
+
+def cpu_baseline(batch, budget_s):
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    q, kc, vc, bt, sl = batch.numpy()
+    spec = batch.spec
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, kc, vc, bt, sl, spec.scale, dtype=spec.dtype, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 2000:
+            break
+    return {"value": round(spec.kv_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} full step(s) of {spec.name} (all {spec.num_q_heads} heads, "
+                      f"{int(spec.seq_lens.sum())} tokens) in fp64 C, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_100k_gqa8")
+    ap.add_argument("--partition-size", type=int, default=1024)
+    ap.add_argument("--variant", choices=["v2", "v1"], default="v2")
+    ap.add_argument("--copies", type=int, default=6)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other-variant timings")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the op shards by "
+              "sequence / kv head / context with no change to the kernels; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spec = wl.config(args.workload)
+    P = args.partition_size
+    batch = wl.generate(spec)
+    S, Hq, D = spec.num_seqs, spec.num_q_heads, spec.head_dim
+    q = batch.query.to(dev)
+    bt = batch.block_tables.to(dev)
+    sl = batch.seq_lens.to(dev)
+    kcs = [batch.key_cache.to(dev)]
+    vcs = [batch.value_cache.to(dev)]
+    for _ in range(args.copies - 1):
+        kcs.append(kcs[0].clone())
+        vcs.append(vcs[0].clone())
+    out = torch.empty_like(q)
+    ws = pa.new_workspace(S, Hq, D, spec.max_seq_len, P, device=dev)
+    L = spec.max_seq_len
+    stream = torch.cuda.current_stream()
+
+    def step(i, variant=args.variant, part=P, wsp=ws):
+        c = i % len(kcs)
+        if variant == "v2":
+            pa.pa_decode_v2(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, part, wsp)
+        else:
+            pa.pa_decode_v1(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L)
+
+    # Parity of the timed configuration on sampled rows, before any timing.
+    import oracle
+    step(0)
+    torch.cuda.synchronize()
+    rows = np.array([(s, h) for s in range(S) for h in range(0, Hq, max(1, Hq // 8))], np.int32)
+    ref = oracle.decode(*batch.numpy(), spec.scale, dtype=spec.dtype, rows=rows)
+    got = out.double().cpu().numpy()[rows[:, 0], rows[:, 1]]
+    err = np.abs(got - ref)
+    assert np.all(err <= 2e-2 + 1e-2 * np.abs(ref)), f"bench parity failed: {err.max()}"
+    print(f"[bench] parity on {len(rows)} rows: max abs err {err.max():.3e}", file=sys.stderr,
+          flush=True)
+
+    # Calibration copy for the HBM counters: a plain 256 MiB device-to-device copy.
+    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    for _ in range(3):
+        cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = max(ms_wall, ms_event)
+    value = spec.kv_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {args.variant} P={P}: {ms_per_step * 1e3:.2f} us/step "
+          f"(wall {ms_wall * 1e3:.2f}, events {ms_event * 1e3:.2f}), {value:.1f} GB/s",
+          file=sys.stderr, flush=True)
+
+    # Dominant kernel alone (V2 Phase 1), one event pair per launch on the launch stream.
+    n1 = max(20, min(args.steps, 100))
+    durs = []
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n1)]
+    for i in range(5):
+        c = i % len(kcs)
+        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+    for i, (a, b) in enumerate(pairs):
+        c = i % len(kcs)
+        a.record(stream)
+        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e3 for a, b in pairs]  # us
+    p1_us = statistics.mean(durs)
+    alg_bytes, kv_bytes = phase1_bytes(spec, P)
+    achieved = alg_bytes / (p1_us * 1e-6) / 1e9
+    traffic = load_traffic(args.workload, P)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                "kernel": "attend_kernel<bf16,128,4,false> (V2 Phase 1)",
+                "launch_us_mean": round(p1_us, 2),
+                "launch_us_p10_p90": [round(float(np.percentile(durs, 10)), 2),
+                                      round(float(np.percentile(durs, 90)), 2)],
+                "algorithmic_bytes_per_launch": alg_bytes}
+
+    # Phase 2 alone.
+    pairs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(20)]
+    for a, b in pairs2:
+        a.record(stream)
+        pa.pa_decode_v2_reduce(out, sl, L, P, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    p2_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in pairs2)
+
+    extras = {}
+    if not args.no_extras and args.variant == "v2":
+        for other in (512, 1024, 2048):
+            if other == P:
+                continue
+            ws2 = pa.new_workspace(S, Hq, D, L, other, device=dev)
+            for i in range(5):
+                step(i, "v2", other, ws2)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(50):
+                step(i, "v2", other, ws2)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 50
+            extras[f"v2_p{other}_us_per_step"] = round(us, 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step(0, "v1")
+        e0.record(stream)
+        for i in range(3):
+            step(i, "v1")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extras["v1_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 3, 1)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(batch, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2), "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) bf16 keys/values/query, random block permutation)",
+        "config": {"workload": spec.name, "num_seqs": S, "seq_len": int(spec.seq_lens[0]),
+                   "q_heads": Hq, "kv_heads": spec.num_kv_heads, "head_dim": D, "block_size": 16,
+                   "partition_size": P, "variant": args.variant, "kv_copies": len(kcs),
+                   "kv_bytes_per_step": spec.kv_bytes},
+        "phase2_us": round(p2_us, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "device": torch.cuda.get_device_name(0),
+        "kernel_sha": kernel_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

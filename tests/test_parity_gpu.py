@@ -181,7 +181,11 @@ def test_phase2_alone_on_oracle_partials():
     pa.pa_decode_v2_reduce(out, db.seq_lens, db.max_seq_len, P, ws)
     g = to_f64(out)
     err = np.abs(g - ref)
-    assert np.all(err <= 1e-6 * np.maximum(np.abs(ref), 1e-3)), float(err.max())
+    # float32 rounding bound: the merge sums weighted partial outputs of either sign, so
+    # its error scales with sum_p (w_p / W) |o_p|, the same merge over |o_p|.
+    mag = oracle.merge(np.abs(f32[0]).astype(np.float64), *(x.astype(np.float64) for x in f32[1:]),
+                       sl, P)
+    assert np.all(err <= 4e-6 * mag + 1e-30), float(np.max(err / np.maximum(mag, 1e-30)))
 
 
 def test_dispatch_threshold():
