@@ -60,7 +60,7 @@ def phase1_bytes(spec, P):
 
 
 def load_traffic(workload, P):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{P}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{P}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -174,43 +174,49 @@ def main():
           f"(wall {ms_wall * 1e3:.2f}, events {ms_event * 1e3:.2f}), {value:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    # Dominant kernel alone (V2 Phase 1), one event pair per launch on the launch stream.
+    # Dominant kernel alone (V2 Phase 1) on the launch stream: an event pair around
+    # n1 back-to-back launches gives the mean duration; one pair per launch gives the spread.
     n1 = max(20, min(args.steps, 100))
-    durs = []
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(n1)]
     for i in range(5):
         c = i % len(kcs)
         pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n1):
+        c = i % len(kcs)
+        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    p1_us = e0.elapsed_time(e1) * 1e3 / n1
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n1)]
     for i, (a, b) in enumerate(pairs):
         c = i % len(kcs)
         a.record(stream)
         pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
         b.record(stream)
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e3 for a, b in pairs]  # us
-    p1_us = statistics.mean(durs)
+    durs = [a.elapsed_time(b) * 1e3 for a, b in pairs]  # us, includes per-pair event overhead
     alg_bytes, kv_bytes = phase1_bytes(spec, P)
     achieved = alg_bytes / (p1_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, P)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "kernel": "attend_kernel<bf16,128,4,false> (V2 Phase 1)",
+                "kernel": "attend_kernel<bf16,128,...,false> (V2 Phase 1)",
                 "launch_us_mean": round(p1_us, 2),
-                "launch_us_p10_p90": [round(float(np.percentile(durs, 10)), 2),
-                                      round(float(np.percentile(durs, 90)), 2)],
+                "launch_us_p10_p90_single": [round(float(np.percentile(durs, 10)), 2),
+                                             round(float(np.percentile(durs, 90)), 2)],
                 "algorithmic_bytes_per_launch": alg_bytes}
 
-    # Phase 2 alone.
-    pairs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(20)]
-    for a, b in pairs2:
-        a.record(stream)
+    # Phase 2 alone: back-to-back launches between one event pair.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(50):
         pa.pa_decode_v2_reduce(out, sl, L, P, ws)
-        b.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    p2_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in pairs2)
+    p2_us = e0.elapsed_time(e1) * 1e3 / 50
 
     extras = {}
     if not args.no_extras and args.variant == "v2":

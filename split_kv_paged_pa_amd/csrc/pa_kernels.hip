@@ -43,6 +43,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -57,30 +59,41 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// max over lanes l, l^16, l^32, l^48 (the four rows of a column), on the
+// gfx950 permlane swaps: permlane32_swap(v, v) returns {v[l % 32], v[l % 32 + 32]}
+// and permlane16_swap(v, v) returns the two rows of each row pair.
+__device__ __forceinline__ float column_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float column_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     return v;
 }
 
-// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even, two per instruction).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ s16x4 pack_bf16_rne(float a, float b, float c, float d) {
-    u32x2 w = {bf16_rne(a) | (bf16_rne(b) << 16), bf16_rne(c) | (bf16_rne(d) << 16)};
-    return __builtin_bit_cast(s16x4, w);
+__device__ __forceinline__ s16x4 pack_bf16(float a, float b, float c, float d) {
+    return __builtin_bit_cast(s16x4, u32x2{pack2_bf16(a, b), pack2_bf16(c, d)});
 }
 
-// Values that are already bf16 numbers held in float32: keep the top half.
-__device__ __forceinline__ s16x4 pack_bf16_exact(f32x4 v) {
-    u32x2 w = {(__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u),
-               (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u)};
-    return __builtin_bit_cast(s16x4, w);
-}
+__device__ __forceinline__ s16x4 pack_bf16(f32x4 v) { return pack_bf16(v[0], v[1], v[2], v[3]); }
 
 __device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.x, v.y}); }
 __device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
@@ -107,12 +120,12 @@ template <> struct Mma<uint16_t> {
     static __device__ __forceinline__ Consts consts(int l16, int grp) {
         float e[4];
         for (int i = 0; i < 4; ++i) e[i] = (4 * grp + i == l16) ? 1.f : 0.f;
-        return {pack_bf16_rne(e[0], e[1], e[2], e[3])};
+        return {pack_bf16(e[0], e[1], e[2], e[3])};
     }
 
     struct Probs { s16x4 p; };
     static __device__ __forceinline__ Probs probs(const float *p) {
-        return {pack_bf16_rne(p[0], p[1], p[2], p[3])};
+        return {pack_bf16(p[0], p[1], p[2], p[3])};
     }
 
     // acc[h] (lane (g, grp), register r) += sum_t P[g][t] V[t][c*32 + grp*8 + 4h + r].
@@ -121,14 +134,17 @@ template <> struct Mma<uint16_t> {
         // Transpose: T[t][j] = V[t][d(j)], lane (j, grp) register r = token 4*grp + r.
         f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo_half(v), k.ident, zero, 0, 0, 0);
         f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi_half(v), k.ident, zero, 0, 0, 0);
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16_exact(t0), pr.p, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16_exact(t1), pr.p, acc[1], 0, 0, 0);
+        // t0/t1 hold bf16 values exactly, so the conversion back is exact.
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16(t0), pr.p, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16(t1), pr.p, acc[1], 0, 0, 0);
     }
 
     static __device__ __forceinline__ float to_float(uint16_t x) {
         return __uint_as_float((uint32_t)x << 16);
     }
-    static __device__ __forceinline__ uint16_t from_float(float x) { return (uint16_t)bf16_rne(x); }
+    static __device__ __forceinline__ uint16_t from_float(float x) {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
 };
 
 // float32 storage: v_mfma_f32_16x16x4_f32, one value per lane per MFMA.
@@ -176,7 +192,7 @@ template <> struct Mma<float> {
 // writes that partition's partials.  V1 (kFinal = true): one workgroup per
 // (kv head, sequence) covers the whole sequence and writes the output.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, bool kFinal>
+template <typename T, int D, int NW, int U, bool kFinal>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
@@ -196,7 +212,10 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __shared__ float sm_o[NW][16][LDS_STRIDE];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    // Wave index, made provably uniform so that everything derived from it (the
+    // block ids in particular) lives in scalar registers and is read with scalar
+    // loads, which do not wait on the vector-memory counter of the K/V loads.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15;
     const int grp = lane >> 4;
     const int p = blockIdx.x;
@@ -235,56 +254,99 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
     const size_t slab = (size_t)kBlockTokens * D;  // elements of one (block, kv head) slab
+    const size_t lane_off = (size_t)l16 * ROW16 + grp;  // this lane's first uint4 in a slab
 
-    for (int j = j_begin + w; j < j_end; j += NW) {
-        const int phys = __builtin_amdgcn_readfirstlane(bt[j]);
-        if ((unsigned)phys >= (unsigned)num_blocks) continue;  // out-of-contract id: skip block
-        const uint4 *kp = reinterpret_cast<const uint4 *>(
-                              key_cache + ((size_t)phys * num_kv_heads + kvh) * slab) +
-                          l16 * ROW16 + grp;
-        const uint4 *vp = reinterpret_cast<const uint4 *>(
-                              value_cache + ((size_t)phys * num_kv_heads + kvh) * slab) +
-                          l16 * ROW16 + grp;
-        uint4 kr[NC], vr[NC];
+    // Wave w takes blocks j0 + i*NW, i = 0 .. nb-1.  Loads run U-1 blocks ahead of
+    // the math in a ring of register slots; the next block id is read one issue
+    // ahead with a scalar load.  Every issue emits the same loads in the same
+    // order -- past the end, or for a block id outside [0, num_blocks), they read
+    // the (cached) query row instead and the block is not attended -- so the
+    // compiler can keep exactly the younger slots outstanding at each wait.
+    const int j0 = j_begin + w;
+    const int nb = j0 < j_end ? (j_end - j0 + NW - 1) / NW : 0;
+    uint4 kb[U][NC], vb[U][NC];
+    bool live[U];
+    int id_next = nb > 0 ? bt[j0] : 0;
+    const uint4 *dummy = reinterpret_cast<const uint4 *>(
+        query + ((size_t)s * num_q_heads + (size_t)kvh * group) * D);
+
+    auto issue = [&](int i, uint4 (&kr)[NC], uint4 (&vr)[NC]) -> bool {
+        const int phys = id_next;
+        id_next = (i + 1 < nb) ? bt[j0 + (i + 1) * NW] : 0;
+        const bool ok = i < nb && (unsigned)phys < (unsigned)num_blocks;
+        const size_t base = ok ? ((size_t)phys * num_kv_heads + kvh) * slab : 0;
+        const uint4 *kp = ok ? reinterpret_cast<const uint4 *>(key_cache + base) + lane_off : dummy;
+        const uint4 *vp = ok ? reinterpret_cast<const uint4 *>(value_cache + base) + lane_off : dummy;
 #pragma unroll
         for (int c = 0; c < NC; ++c) kr[c] = kp[c * 4];
 #pragma unroll
         for (int c = 0; c < NC; ++c) vr[c] = vp[c * 4];
+        return ok;
+    };
 
-        const int valid = t_end - j * kBlockTokens;  // tokens of this block in range (>= 1)
-
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // One block: logits, running-max update, weights, PV.  kTail: the block
+    // holds the end of the token range, so some of its slots are masked.
+    auto attend = [&](auto tail, int i, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+        constexpr bool kTail = decltype(tail)::value;
+        const int valid = t_end - (j0 + i * NW) * kBlockTokens;  // tokens in range (>= 1)
+        // Two independent MFMA chains (even / odd chunks) halve the dependent latency.
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) M::qk(sacc, kr[c], qv[c]);
+        for (int c = 0; c < NC; c += 2) {
+            M::qk(s0, kr[c], qv[c]);
+            if (c + 1 < NC) M::qk(s1, kr[c + 1], qv[c + 1]);
+        }
+        const f32x4 sacc = s0 + s1;
 
         float z[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * scale : -INFINITY;
-        float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = fmaxf(m_run, bm);
-        const float alpha = exp_e(m_run - m_new);
+        for (int r = 0; r < 4; ++r)
+            z[r] = (!kTail || 4 * grp + r < valid) ? sacc[r] * scale : -INFINITY;
+        const float bm = column_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+        // Rescale only when some column's max grew: otherwise the factor is
+        // exactly 1 and skipping it changes no bit.
+        if (__builtin_amdgcn_ballot_w64(bm > m_run) != 0) {
+            const float m_new = fmaxf(m_run, bm);
+            const float alpha = exp_e(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        }
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = exp_e(z[i] - m_new);
-        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+        for (int r = 0; r < 4; ++r) pr[r] = exp_e(z[r] - m_run);
+        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-        if (l16 >= valid) {
+        if (kTail && l16 >= valid) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) vr[c] = make_uint4(0, 0, 0, 0);
         }
         const typename M::Probs pb = M::probs(pr);
 #pragma unroll
         for (int c = 0; c < NC; ++c) M::pv(&acc[c * M::kTiles], vr[c], kc, pb);
+    };
+    auto step = [&](int i, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+        if ((j0 + i * NW + 1) * kBlockTokens <= t_end)
+            attend(std::false_type{}, i, kr, vr);
+        else
+            attend(std::true_type{}, i, kr, vr);
+    };
+
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) live[u] = issue(u, kb[u], vb[u]);
+    for (int i0 = 0; i0 < nb; i0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            constexpr int kAhead = U - 1;
+            const int slot = (u + kAhead) % U;
+            live[slot] = issue(i0 + u + kAhead, kb[slot], vb[slot]);
+            if (live[u]) step(i0 + u, kb[u], vb[u]);
+        }
     }
 
     // Full exp-sum of column g over the wave.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = column_sum(l_run);
 
     // Publish the wave's state: lane (g, grp) owns d = c*4E + grp*E + [0, E).
     if (grp == 0) {
@@ -341,20 +403,25 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: one workgroup (4 waves) per (query head, sequence).  Each wave takes
-// partitions p = w, w + 4, ...; lane l holds d = l*DPL .. l*DPL + DPL - 1.
+// Phase 2: one workgroup of NW waves per (query head, sequence).  The max logits
+// and exp-sums of up to CH partitions are staged in LDS while the global max is
+// found; then wave w sums partitions p = w, w + NW, ... with eight loads in
+// flight per lane; lane l holds d = l*DPL .. l*DPL + DPL - 1.  Waves combine in
+// a fixed order, so the result is reproducible bit for bit.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void reduce_kernel(
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void reduce_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
     int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
     using M = Mma<T>;
-    constexpr int NW = 4;
+    constexpr int NT = NW * 64;
     constexpr int DPL = D / 64;
-    constexpr int CH = 1024;  // partitions staged per round
+    constexpr int CH = 2048;  // partitions staged per round
+    constexpr int UNR = 8;    // partition rows in flight per lane
+    __shared__ float sm_m[CH];
+    __shared__ float sm_e[CH];
     __shared__ float sm_red[NW];
-    __shared__ float sm_w[CH];
     __shared__ float sm_acc[NW][D];
     __shared__ float sm_wsum[NW];
 
@@ -369,7 +436,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
     if (parts == 0) {
-        for (int d = tid; d < D; d += 256) orow[d] = M::from_float(0.f);
+        for (int d = tid; d < D; d += NT) orow[d] = M::from_float(0.f);
         return;
     }
     const float *ml = max_logits + head * max_parts;
@@ -377,13 +444,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const float *po = tmp_out + head * max_parts * D;
 
     float mx = -INFINITY;
-    for (int i = tid; i < parts; i += 256) mx = fmaxf(mx, ml[i]);
+    for (int i = tid; i < parts; i += NT) {
+        const float m = ml[i];
+        mx = fmaxf(mx, m);
+        if (i < CH) {
+            sm_m[i] = m;
+            sm_e[i] = es[i];
+        }
+    }
     mx = wave_max(mx);
     if (lane == 0) sm_red[w] = mx;
     __syncthreads();
-    mx = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+    mx = sm_red[0];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, sm_red[ww]);
     if (mx == -INFINITY) {  // only reachable when no block id of the sequence was valid
-        for (int d = tid; d < D; d += 256) orow[d] = M::from_float(0.f);
+        for (int d = tid; d < D; d += NT) orow[d] = M::from_float(0.f);
         return;
     }
 
@@ -393,54 +469,64 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     float wsum = 0.f;
     for (int p0 = 0; p0 < parts; p0 += CH) {
         const int n = min(CH, parts - p0);
-        __syncthreads();
-        for (int i = tid; i < n; i += 256) sm_w[i] = exp_e(ml[p0 + i] - mx) * es[p0 + i];
-        __syncthreads();
-        int i = w;
-        for (; i + 3 * NW < n; i += 4 * NW) {
-            float wt[4];
-            float vals[4][DPL];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                wt[u] = sm_w[i + u * NW];
-                const float *src = po + (size_t)(p0 + i + u * NW) * D + lane * DPL;
-#pragma unroll
-                for (int k = 0; k < DPL; ++k) vals[u][k] = src[k];
+        if (p0 > 0) {
+            __syncthreads();
+            for (int i = tid; i < n; i += NT) {
+                sm_m[i] = ml[p0 + i];
+                sm_e[i] = es[p0 + i];
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                wsum += wt[u];
-#pragma unroll
-                for (int k = 0; k < DPL; ++k) acc[k] += wt[u] * vals[u][k];
-            }
+            __syncthreads();
         }
-        for (; i < n; i += NW) {
-            const float wt = sm_w[i];
-            const float *src = po + (size_t)(p0 + i) * D + lane * DPL;
-            wsum += wt;
+        for (int i = w; i < n; i += UNR * NW) {
+            float vals[UNR][DPL];
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) acc[k] += wt * src[k];
+            for (int u = 0; u < UNR; ++u) {
+                const int idx = i + u * NW;
+                if (idx < n) {
+                    const float *src = po + (size_t)(p0 + idx) * D + lane * DPL;
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) vals[u][k] = src[k];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int idx = i + u * NW;
+                if (idx < n) {
+                    const float wt = exp_e(sm_m[idx] - mx) * sm_e[idx];
+                    wsum += wt;
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) acc[k] += wt * vals[u][k];
+                }
+            }
         }
     }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) sm_acc[w][lane * DPL + k] = acc[k];
     if (lane == 0) sm_wsum[w] = wsum;
     __syncthreads();
-    const float total = (sm_wsum[0] + sm_wsum[1]) + (sm_wsum[2] + sm_wsum[3]);
+    float total = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) total += sm_wsum[ww];
     const float inv = 1.f / total;
-    for (int d = tid; d < D; d += 256) {
-        const float o = (sm_acc[0][d] + sm_acc[1][d]) + (sm_acc[2][d] + sm_acc[3][d]);
+    for (int d = tid; d < D; d += NT) {
+        float o = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) o += sm_acc[ww][d];
         orow[d] = M::from_float(o * inv);
     }
 }
 
 constexpr int kWaves = 4;
+constexpr int kReduceWaves = 16;
+
+// Blocks in flight per wave: three when a block's K and V fit in 32 VGPRs.
+template <typename T, int D> constexpr int prefetch_depth() { return D * sizeof(T) <= 256 ? 3 : 2; }
 
 template <typename T, int D, bool kFinal>
 hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
     const int group = pb.num_q_heads / pb.num_kv_heads;
     dim3 grid(kFinal ? 1 : parts->max_parts, pb.num_kv_heads, pb.num_seqs);
-    attend_kernel<T, D, kWaves, kFinal><<<grid, kWaves * 64, 0, stream>>>(
+    attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), kFinal><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
         pb.num_kv_heads, group, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
@@ -464,7 +550,7 @@ template <typename T, int D>
 hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_heads, int max_seq_len,
                            const Partials &parts, void *out, hipStream_t stream) {
     dim3 grid(num_q_heads, num_seqs);
-    reduce_kernel<T, D><<<grid, 256, 0, stream>>>(parts.tmp_out, parts.exp_sums, parts.max_logits,
+    reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(parts.tmp_out, parts.exp_sums, parts.max_logits,
                                                   seq_lens, num_q_heads, max_seq_len,
                                                   parts.partition_size, parts.max_parts,
                                                   static_cast<T *>(out));

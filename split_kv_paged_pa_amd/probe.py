@@ -1,0 +1,54 @@
+"""Binding of libpa_probe.so: an HBM read-bandwidth probe with the decode
+kernels' access shape (measurement only; not part of the attention ABI)."""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa_probe.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python split_kv_paged_pa_amd/build.py`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.pa_probe_read.argtypes = [P, P, I, I, I, I, I, P, P]
+        lib.pa_probe_read.restype = I
+        _lib = lib
+    return _lib
+
+
+def read_bandwidth(buf: torch.Tensor, chunk_ids, chunk_bytes=4096, waves_per_group=4,
+                   num_groups=1024, reps=20, stream=None, shape=0):
+    """GB/s of reading the chunks of `buf` (a GPU tensor) listed in chunk_ids
+    (int32 GPU tensor, or None for all chunks in order), timed with HIP events
+    over `reps` launches on `stream`.  shape 0: 1 KiB contiguous per load
+    instruction; shape 1: the attention kernels' 16-rows-by-64-bytes shape."""
+    nbytes = buf.numel() * buf.element_size()
+    n = nbytes // chunk_bytes if chunk_ids is None else chunk_ids.numel()
+    if chunk_ids is not None:
+        assert chunk_ids.dtype == torch.int32 and chunk_ids.is_cuda
+        hi = int(chunk_ids.max().item())
+        lo = int(chunk_ids.min().item())
+        assert lo >= 0 and (hi + 1) * chunk_bytes <= nbytes, "chunk ids out of range"
+    sink = torch.empty(num_groups * waves_per_group * 64, dtype=torch.int32, device=buf.device)
+    st = stream or torch.cuda.current_stream()
+    args = (ctypes.c_void_p(buf.data_ptr()),
+            ctypes.c_void_p(0 if chunk_ids is None else chunk_ids.data_ptr()), int(n),
+            int(chunk_bytes), int(waves_per_group), int(num_groups), int(shape),
+            ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+    lib = _load()
+    assert lib.pa_probe_read(*args) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        assert lib.pa_probe_read(*args) == 0
+    e1.record(st)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    return n * chunk_bytes / sec / 1e9
