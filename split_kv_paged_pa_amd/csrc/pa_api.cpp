@@ -4,6 +4,7 @@
 // synchronises or reads device memory.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -20,7 +21,36 @@ constexpr int kMaxGridYZ = 65535;
 constexpr int kV2MinSeqLen = 8192;
 constexpr size_t kAlign = 256;
 
+// Phase 1 groups consecutive partitions of one (sequence, kv head) into one
+// workgroup when there are few partitions overall (at most kGroupFewUnits per
+// compute unit): one long-running workgroup per compute unit streams faster on
+// MI355X than two shorter ones sharing a unit.
+constexpr int kGroupFewUnits = 4;
+constexpr int kMaxDevices = 64;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int compute_units() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    if (n > 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Partitions per Phase-1 workgroup for S * Hkv * P_max units.
+int partitions_per_group(long long units) {
+    const int cus = compute_units();
+    if (cus <= 0 || units <= cus || units > (long long)kGroupFewUnits * cus) return 1;
+    return (int)((units + cus - 1) / cus);
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -95,9 +125,10 @@ pa::Problem make_problem(const void *query, const void *key_cache, const void *v
     return pb;
 }
 
-// Checks the V2 workspace and carves it; *empty is set when nothing needs launching.
-pa_status_t carve(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, int partition_size,
-                  void *workspace, size_t workspace_bytes, pa::Partials *parts) {
+// Checks the V2 workspace and carves it.
+pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                  int partition_size, void *workspace, size_t workspace_bytes,
+                  pa::Partials *parts) {
     if (partition_size < kBlockTokens || partition_size % kBlockTokens != 0)
         return PA_ERR_UNSUPPORTED;
     if ((long long)max_seq_len + partition_size > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
@@ -113,6 +144,7 @@ pa_status_t carve(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, 
     parts->max_logits = reinterpret_cast<float *>(base + lay.max_off);
     parts->partition_size = partition_size;
     parts->max_parts = lay.max_parts;
+    parts->per_group = partitions_per_group((long long)num_seqs * num_kv_heads * lay.max_parts);
     return PA_OK;
 }
 
@@ -190,8 +222,8 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                    max_blocks_per_seq, max_seq_len, scale, dtype);
     if (st != PA_OK) return st;
     pa::Partials parts;
-    st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, workspace,
-               workspace_bytes, &parts);
+    st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
+               workspace, workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0 || parts.max_parts == 0) return st;
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -209,7 +241,7 @@ pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
     pa::Partials parts;
-    pa_status_t st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size,
+    pa_status_t st = carve(num_seqs, num_q_heads, 1, head_dim, max_seq_len, partition_size,
                            const_cast<void *>(workspace), workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (!out || !seq_lens) return PA_ERR_NULL_POINTER;
@@ -229,8 +261,8 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                                    max_blocks_per_seq, max_seq_len, scale, dtype);
     if (st != PA_OK) return st;
     pa::Partials parts;
-    st = carve(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, workspace,
-               workspace_bytes, &parts);
+    st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
+               workspace, workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (!out) return PA_ERR_NULL_POINTER;
     hipStream_t hs = static_cast<hipStream_t>(stream);

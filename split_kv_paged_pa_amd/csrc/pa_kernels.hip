@@ -188,17 +188,19 @@ template <> struct Mma<float> {
 };
 
 // ---------------------------------------------------------------------------
-// Phase 1 (kFinal = false): one workgroup per (partition p, kv head, sequence)
-// writes that partition's partials.  V1 (kFinal = true): one workgroup per
-// (kv head, sequence) covers the whole sequence and writes the output.
+// Phase 1 (kFinal = false): workgroup (pg, kv head, sequence) handles the
+// partitions p in [pg * ppw, min((pg + 1) * ppw, ceil(L / P))) of that sequence
+// and kv head, one after the other, and writes each one's partials.  V1
+// (kFinal = true): workgroup (0, kv head, sequence) covers the whole sequence
+// as a single partition and writes the output.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW, int U, bool kFinal>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
     int num_kv_heads, int group, int num_blocks, int max_blocks, int max_seq_len, float scale,
-    int partition_size, int max_parts, float *__restrict__ tmp_out, float *__restrict__ exp_sums,
-    float *__restrict__ max_logits, T *__restrict__ out) {
+    int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
+    float *__restrict__ exp_sums, float *__restrict__ max_logits, T *__restrict__ out) {
     using M = Mma<T>;
     constexpr int E = M::E;
     constexpr int NC = D / (4 * E);          // 16-byte chunks per lane per row
@@ -218,19 +220,25 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15;
     const int grp = lane >> 4;
-    const int p = blockIdx.x;
     const int kvh = blockIdx.y;
     const int s = blockIdx.z;
 
     const int L = min(max(seq_lens[s], 0), max_seq_len);
-    int t_begin = 0, t_end = L;
-    if (!kFinal) {
-        t_begin = p * partition_size;
-        if (t_begin >= L) return;  // uniform over the workgroup
-        t_end = min(t_begin + partition_size, L);
+    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    // Partitions of this workgroup, in blocks of bp each.
+    int bp, p_begin, p_end;
+    if (kFinal) {
+        bp = max(nblk, 1);
+        p_begin = 0;
+        p_end = 1;
+    } else {
+        bp = partition_size / kBlockTokens;
+        const int parts = (nblk + bp - 1) / bp;
+        p_begin = blockIdx.x * ppw;
+        p_end = min(p_begin + ppw, parts);
+        if (p_begin >= p_end) return;  // uniform over the workgroup
     }
-    const int j_begin = t_begin / kBlockTokens;
-    const int j_end = (t_end + kBlockTokens - 1) / kBlockTokens;
+    auto part_end = [&](int p) { return min((p + 1) * bp, nblk); };  // end block of partition p
 
     // Q^T operand: lane (g, grp) holds chunk c of query head kvh*G + g (zero for g >= G).
     const int g = l16;
@@ -250,30 +258,43 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     float l_run = 0.f;        // this lane's share of the running exp-sum
     f32x4 acc[NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
-    const size_t slab = (size_t)kBlockTokens * D;  // elements of one (block, kv head) slab
+    const size_t slab = (size_t)kBlockTokens * D;        // elements of one (block, kv head) slab
     const size_t lane_off = (size_t)l16 * ROW16 + grp;  // this lane's first uint4 in a slab
-
-    // Wave w takes blocks j0 + i*NW, i = 0 .. nb-1.  Loads run U-1 blocks ahead of
-    // the math in a ring of register slots; the next block id is read one issue
-    // ahead with a scalar load.  Every issue emits the same loads in the same
-    // order -- past the end, or for a block id outside [0, num_blocks), they read
-    // the (cached) query row instead and the block is not attended -- so the
-    // compiler can keep exactly the younger slots outstanding at each wait.
-    const int j0 = j_begin + w;
-    const int nb = j0 < j_end ? (j_end - j0 + NW - 1) / NW : 0;
-    uint4 kb[U][NC], vb[U][NC];
-    bool live[U];
-    int id_next = nb > 0 ? bt[j0] : 0;
     const uint4 *dummy = reinterpret_cast<const uint4 *>(
         query + ((size_t)s * num_q_heads + (size_t)kvh * group) * D);
 
-    auto issue = [&](int i, uint4 (&kr)[NC], uint4 (&vr)[NC]) -> bool {
+    // ---- issue side: wave w takes blocks p*bp + w, p*bp + w + NW, ... of each of
+    // the workgroup's partitions p in turn; loads run U-1 blocks ahead of the math
+    // in a ring of register slots, across partition boundaries.  The next block
+    // id is read one issue ahead with a scalar load.
+    int i_p = p_begin;                 // partition of the next block to issue (p_end: done)
+    int i_j = p_begin * bp + w;        // next block to issue
+    auto settle = [&]() {
+        while (i_p < p_end && i_j >= part_end(i_p)) {
+            ++i_p;
+            i_j = i_p * bp + w;
+        }
+    };
+    settle();
+    int id_next = i_p < p_end ? bt[i_j] : 0;
+
+    // Every issue emits the same loads in the same order -- past the end, or for
+    // a block id outside [0, num_blocks), they read the (cached) query row and the
+    // block is not attended -- so the compiler keeps exactly the younger ring
+    // slots outstanding at each wait.
+    auto issue = [&](uint4 (&kr)[NC], uint4 (&vr)[NC], int &part, int &blk) -> bool {
+        part = i_p;
+        blk = i_j;
         const int phys = id_next;
-        id_next = (i + 1 < nb) ? bt[j0 + (i + 1) * NW] : 0;
-        const bool ok = i < nb && (unsigned)phys < (unsigned)num_blocks;
+        const bool ok = i_p < p_end && (unsigned)phys < (unsigned)num_blocks;
+        if (i_p < p_end) {
+            i_j += NW;
+            settle();
+            id_next = i_p < p_end ? bt[i_j] : 0;
+        }
         const size_t base = ok ? ((size_t)phys * num_kv_heads + kvh) * slab : 0;
         const uint4 *kp = ok ? reinterpret_cast<const uint4 *>(key_cache + base) + lane_off : dummy;
         const uint4 *vp = ok ? reinterpret_cast<const uint4 *>(value_cache + base) + lane_off : dummy;
@@ -285,10 +306,10 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     };
 
     // One block: logits, running-max update, weights, PV.  kTail: the block
-    // holds the end of the token range, so some of its slots are masked.
-    auto attend = [&](auto tail, int i, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+    // holds the end of the sequence, so some of its slots are masked.
+    auto attend = [&](auto tail, int j, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
         constexpr bool kTail = decltype(tail)::value;
-        const int valid = t_end - (j0 + i * NW) * kBlockTokens;  // tokens in range (>= 1)
+        const int valid = L - j * kBlockTokens;  // tokens of the block in range (>= 1)
         // Two independent MFMA chains (even / odd chunks) halve the dependent latency.
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -326,80 +347,101 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c) M::pv(&acc[c * M::kTiles], vr[c], kc, pb);
     };
-    auto step = [&](int i, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
-        if ((j0 + i * NW + 1) * kBlockTokens <= t_end)
-            attend(std::false_type{}, i, kr, vr);
+    auto step = [&](int j, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+        if ((j + 1) * kBlockTokens <= L)
+            attend(std::false_type{}, j, kr, vr);
         else
-            attend(std::true_type{}, i, kr, vr);
+            attend(std::true_type{}, j, kr, vr);
     };
 
+    // End of partition p: merge the waves' states (fixed order) and write.
+    auto finish = [&](int p) {
+        const float l_col = column_sum(l_run);
+        __syncthreads();  // the previous partition's readers are done with the LDS
+        // lane (g, grp) owns d = c*4E + grp*E + [0, E).
+        if (grp == 0) {
+            sm_m[w][g] = m_run;
+            sm_l[w][g] = l_col;
+        }
 #pragma unroll
-    for (int u = 0; u < U - 1; ++u) live[u] = issue(u, kb[u], vb[u]);
-    for (int i0 = 0; i0 < nb; i0 += U) {
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int t = 0; t < M::kTiles; ++t) {
+                float *dst = &sm_o[w][g][c * 4 * E + grp * E + t * 4];
+                *reinterpret_cast<f32x4 *>(dst) = acc[c * M::kTiles + t];
+            }
+        }
+        __syncthreads();
+        const size_t head0 = (size_t)s * num_q_heads + (size_t)kvh * group;
+        // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
+        if (threadIdx.x < 16) {
+            const int gg = threadIdx.x;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[ww][gg]);
+            float f[NW];
+            float total = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[ww][gg] - mx);
+                total += f[ww] * sm_l[ww][gg];
+            }
+            const float inv = total > 0.f ? 1.f / total : 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
+            if (!kFinal && gg < group) {
+                const size_t row = (head0 + gg) * max_parts + p;
+                exp_sums[row] = total;
+                max_logits[row] = mx;
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < group * D; idx += NW * 64) {
+            const int gg = idx / D;
+            const int d = idx - gg * D;
+            float o = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) o += sm_f[ww][gg] * sm_o[ww][gg][d];
+            if (kFinal) {
+                out[(head0 + gg) * D + d] = M::from_float(o);
+            } else {
+                tmp_out[((head0 + gg) * max_parts + p) * D + d] = o;
+            }
+        }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // ---- attend side: consume the ring in order; close each partition when the
+    // next block belongs to a later one.  Every wave closes every partition once,
+    // so the barriers inside finish() line up across the waves.
+    int a_p = p_begin;
+    uint4 kb[U][NC], vb[U][NC];
+    int sp[U], sj[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) live[u] = issue(kb[u], vb[u], sp[u], sj[u]);
+    bool done = false;
+    for (;;) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             constexpr int kAhead = U - 1;
             const int slot = (u + kAhead) % U;
-            live[slot] = issue(i0 + u + kAhead, kb[slot], vb[slot]);
-            if (live[u]) step(i0 + u, kb[u], vb[u]);
+            live[slot] = issue(kb[slot], vb[slot], sp[slot], sj[slot]);  // unconditional
+            if (!done) {
+                if (sp[u] >= p_end) {
+                    done = true;
+                } else {
+                    while (a_p < sp[u]) finish(a_p++);
+                    if (live[u]) step(sj[u], kb[u], vb[u]);
+                }
+            }
         }
+        if (done) break;
     }
-
-    // Full exp-sum of column g over the wave.
-    l_run = column_sum(l_run);
-
-    // Publish the wave's state: lane (g, grp) owns d = c*4E + grp*E + [0, E).
-    if (grp == 0) {
-        sm_m[w][g] = m_run;
-        sm_l[w][g] = l_run;
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int t = 0; t < M::kTiles; ++t) {
-            float *dst = &sm_o[w][g][c * 4 * E + grp * E + t * 4];
-            *reinterpret_cast<f32x4 *>(dst) = acc[c * M::kTiles + t];
-        }
-    }
-    __syncthreads();
-
-    // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
-    if (threadIdx.x < 16) {
-        const int gg = threadIdx.x;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[ww][gg]);
-        float f[NW];
-        float total = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[ww][gg] - mx);
-            total += f[ww] * sm_l[ww][gg];
-        }
-        const float inv = total > 0.f ? 1.f / total : 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
-        if (!kFinal && gg < group) {
-            const size_t row = ((size_t)s * num_q_heads + (size_t)kvh * group + gg) * max_parts + p;
-            exp_sums[row] = total;
-            max_logits[row] = mx;
-        }
-    }
-    __syncthreads();
-
-    for (int idx = threadIdx.x; idx < group * D; idx += NW * 64) {
-        const int gg = idx / D;
-        const int d = idx - gg * D;
-        float o = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) o += sm_f[ww][gg] * sm_o[ww][gg][d];
-        const size_t h = (size_t)s * num_q_heads + (size_t)kvh * group + gg;
-        if (kFinal) {
-            out[h * D + d] = M::from_float(o);
-        } else {
-            tmp_out[(h * max_parts + p) * D + d] = o;
-        }
-    }
+    while (a_p < p_end) finish(a_p++);
 }
 
 // ---------------------------------------------------------------------------
@@ -525,12 +567,13 @@ template <typename T, int D> constexpr int prefetch_depth() { return D * sizeof(
 template <typename T, int D, bool kFinal>
 hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
     const int group = pb.num_q_heads / pb.num_kv_heads;
-    dim3 grid(kFinal ? 1 : parts->max_parts, pb.num_kv_heads, pb.num_seqs);
+    const int ppw = kFinal ? 1 : parts->per_group;
+    dim3 grid(kFinal ? 1 : (parts->max_parts + ppw - 1) / ppw, pb.num_kv_heads, pb.num_seqs);
     attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), kFinal><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
         pb.num_kv_heads, group, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
-        kFinal ? 0 : parts->partition_size, kFinal ? 0 : parts->max_parts,
+        kFinal ? kBlockTokens : parts->partition_size, ppw, kFinal ? 0 : parts->max_parts,
         kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
         kFinal ? nullptr : parts->max_logits, static_cast<T *>(out));
     return hipGetLastError();

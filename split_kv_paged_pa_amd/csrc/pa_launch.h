@@ -30,6 +30,7 @@ struct Partials {
     float *max_logits;   // [S][Hq][max_parts]
     int partition_size;
     int max_parts;
+    int per_group;   // consecutive partitions handled by one Phase-1 workgroup
 };
 
 // V1: one workgroup per (kv head, sequence) over the whole sequence -> out.

@@ -69,6 +69,36 @@ def test_many_partitions_reduce_chunks():
     assert_close(to_f64(out), oracle_out(b), "bf16", "P=16, 1250 partitions")
 
 
+GROUPED = [  # S * Hkv * ceil(max_len / P) between one and four units per compute unit
+    ("one_seq_p512", [20000], 8, 512),
+    ("one_seq_p256", [20000], 8, 256),
+    ("ragged_p256", [20000, 5, 13000], 4, 256),
+    ("ragged_p1024", [100000, 17, 65536, 1], 2, 1024),
+]
+
+
+@pytest.mark.parametrize("name,lens,hkv,P", GROUPED, ids=[g[0] for g in GROUPED])
+def test_grouped_partitions(name, lens, hkv, P):
+    """Phase-1 workgroups that handle several consecutive partitions each."""
+    spec = wl.custom(name, 112, "bf16", hkv * 8, hkv, 128, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    print(f"[case] grouped {name}", flush=True)
+    ref = oracle_out(b)
+    assert_close(to_f64(db.run_v2(P)), ref, "bf16", f"grouped {name}")
+    ws = db.workspace(P)
+    pa.pa_decode_v2_partials(*db.args(), P, ws)
+    tmp, es, ml = (to_f64(x) for x in pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads,
+                                                         spec.head_dim, db.max_seq_len, P))
+    q, kc, vc, bt, sl = b.numpy()
+    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P, dtype="bf16",
+                                     max_partitions=tmp.shape[2])
+    for s, L in enumerate(sl):
+        n = oracle.num_partitions(L, P)
+        assert np.all(np.abs(ml[s, :, :n] - rml[s, :, :n]) <= 1e-5 * (1 + np.abs(rml[s, :, :n])))
+        assert_close(tmp[s, :, :n], rtmp[s, :, :n], "bf16", f"grouped partials s={s}")
+
+
 def test_outlier_keys_stability():
     spec = wl.custom("outliers", 105, "bf16", 16, 2, 128, [5000, 300, 9000],
                      outlier_frac=0.02, outlier_mult=40.0)
