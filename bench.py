@@ -88,6 +88,27 @@ def cpu_baseline(batch, budget_s):
                       f"{int(spec.seq_lens.sum())} tokens) in fp64 C, {el:.1f} s"}
 
 
+def hbm_probe(dev):
+    """Achievable HBM read bandwidth (GB/s) for streaming and for random 4 KiB chunks,
+    measured with libpa_probe.so (no arithmetic): the ceiling Phase 1 can approach.
+    'random' reads 300000 chunks (1.2 GB) drawn from a 4 GiB buffer per launch, so
+    the 256 MB Infinity Cache cannot hold them; 'kernel_shape' reads the same chunks
+    with the attention kernels' 16-rows-by-64-bytes load shape."""
+    from split_kv_paged_pa_amd import probe
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    ids = torch.randperm((4 << 30) // 4096, generator=torch.Generator().manual_seed(0))
+    ids = ids[:300000].to(torch.int32).to(dev)
+    res = {"sequential_4GiB": round(probe.read_bandwidth(buf, None, 4096, 4, 1024, reps=5), 1)}
+    for groups in (196, 392):
+        res[f"random_4KiB_{groups}wg"] = round(
+            probe.read_bandwidth(buf, ids, 4096, 4, groups, reps=5, shape=0), 1)
+        res[f"random_4KiB_{groups}wg_kernel_shape"] = round(
+            probe.read_bandwidth(buf, ids, 4096, 4, groups, reps=5, shape=1), 1)
+    del buf, ids
+    torch.cuda.empty_cache()
+    return {"unit": "GB/s", **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +120,10 @@ def main():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the other-variant timings")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time V2 at other partition sizes and V1 (same workload)")
+    ap.add_argument("--no-extras", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -148,8 +172,9 @@ def main():
     print(f"[bench] parity on {len(rows)} rows: max abs err {err.max():.3e}", file=sys.stderr,
           flush=True)
 
-    # Calibration copy for the HBM counters: a plain 256 MiB device-to-device copy.
-    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    # Calibration copy for the HBM counters: a plain 768 MiB device-to-device copy
+    # (a size no other copy here has, so its dispatches are easy to pick out).
+    cal_src = torch.empty(768 << 20, dtype=torch.uint8, device=dev)
     cal_dst = torch.empty_like(cal_src)
     for _ in range(3):
         cal_dst.copy_(cal_src)
@@ -209,17 +234,8 @@ def main():
                                              round(float(np.percentile(durs, 90)), 2)],
                 "algorithmic_bytes_per_launch": alg_bytes}
 
-    # Phase 2 alone: back-to-back launches between one event pair.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(50):
-        pa.pa_decode_v2_reduce(out, sl, L, P, ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    p2_us = e0.elapsed_time(e1) * 1e3 / 50
-
     extras = {}
-    if not args.no_extras and args.variant == "v2":
+    if args.extras and not args.no_extras and args.variant == "v2":
         for other in (512, 1024, 2048):
             if other == P:
                 continue
@@ -244,6 +260,8 @@ def main():
         torch.cuda.synchronize()
         extras["v1_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 3, 1)
 
+    probe = None if args.no_probe else hbm_probe(dev)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(batch, args.cpu_seconds)
 
     line = {
@@ -256,9 +274,11 @@ def main():
                    "q_heads": Hq, "kv_heads": spec.num_kv_heads, "head_dim": D, "block_size": 16,
                    "partition_size": P, "variant": args.variant, "kv_copies": len(kcs),
                    "kv_bytes_per_step": spec.kv_bytes},
-        "phase2_us": round(p2_us, 2),
+        # Phase 2 and the gap between the launches, as the step sees them.
+        "phase2_us_in_step": round(ms_per_step * 1e3 - p1_us, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_probe": probe,
         "extras": extras,
         "device": torch.cuda.get_device_name(0),
         "kernel_sha": kernel_sha(),

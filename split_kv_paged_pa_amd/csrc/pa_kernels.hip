@@ -445,11 +445,13 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: one workgroup of NW waves per (query head, sequence).  The max logits
-// and exp-sums of up to CH partitions are staged in LDS while the global max is
-// found; then wave w sums partitions p = w, w + NW, ... with eight loads in
-// flight per lane; lane l holds d = l*DPL .. l*DPL + DPL - 1.  Waves combine in
-// a fixed order, so the result is reproducible bit for bit.
+// Phase 2: one workgroup of NW waves per (query head, sequence).  Wave w takes
+// partitions p = w, w + NW, ..., R at a time: it loads their max logits, exp-sums
+// and partial outputs together (lane l holds d = l*DPL .. l*DPL + DPL - 1), and
+// folds them into a wave-local {max, weight sum, weighted output} with the
+// same rescale as Phase 1.  The waves then merge through LDS in a fixed order,
+// so the result is reproducible bit for bit.  For up to NW * R partitions this
+// is a single round of global loads.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void reduce_kernel(
@@ -459,101 +461,89 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     using M = Mma<T>;
     constexpr int NT = NW * 64;
     constexpr int DPL = D / 64;
-    constexpr int CH = 2048;  // partitions staged per round
-    constexpr int UNR = 8;    // partition rows in flight per lane
-    __shared__ float sm_m[CH];
-    __shared__ float sm_e[CH];
-    __shared__ float sm_red[NW];
+    constexpr int R = 8;  // partitions in flight per wave
+    __shared__ float sm_m[NW];
+    __shared__ float sm_w[NW];
     __shared__ float sm_acc[NW][D];
-    __shared__ float sm_wsum[NW];
 
     const int h = blockIdx.x;
     const int s = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t head = (size_t)s * num_q_heads + h;
     T *orow = out + head * D;
 
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
-    if (parts == 0) {
-        for (int d = tid; d < D; d += NT) orow[d] = M::from_float(0.f);
-        return;
-    }
     const float *ml = max_logits + head * max_parts;
     const float *es = exp_sums + head * max_parts;
     const float *po = tmp_out + head * max_parts * D;
 
-    float mx = -INFINITY;
-    for (int i = tid; i < parts; i += NT) {
-        const float m = ml[i];
-        mx = fmaxf(mx, m);
-        if (i < CH) {
-            sm_m[i] = m;
-            sm_e[i] = es[i];
-        }
-    }
-    mx = wave_max(mx);
-    if (lane == 0) sm_red[w] = mx;
-    __syncthreads();
-    mx = sm_red[0];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, sm_red[ww]);
-    if (mx == -INFINITY) {  // only reachable when no block id of the sequence was valid
-        for (int d = tid; d < D; d += NT) orow[d] = M::from_float(0.f);
-        return;
-    }
-
+    float m_w = -INFINITY;  // wave-local running max
+    float wsum = 0.f;       // wave-local sum of exp(m_p - m_w) * s_p
     float acc[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-    float wsum = 0.f;
-    for (int p0 = 0; p0 < parts; p0 += CH) {
-        const int n = min(CH, parts - p0);
-        if (p0 > 0) {
-            __syncthreads();
-            for (int i = tid; i < n; i += NT) {
-                sm_m[i] = ml[p0 + i];
-                sm_e[i] = es[p0 + i];
+    for (int p0 = w; p0 < parts; p0 += R * NW) {
+        float pm[R], ps[R], po_v[R][DPL];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int p = p0 + r * NW;
+            pm[r] = -INFINITY;
+            ps[r] = 0.f;
+            if (p < parts) {
+                pm[r] = ml[p];
+                ps[r] = es[p];
+                const float *src = po + (size_t)p * D + lane * DPL;
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) po_v[r][k] = src[k];
             }
-            __syncthreads();
         }
-        for (int i = w; i < n; i += UNR * NW) {
-            float vals[UNR][DPL];
+        float cm = pm[0];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int idx = i + u * NW;
-                if (idx < n) {
-                    const float *src = po + (size_t)(p0 + idx) * D + lane * DPL;
+        for (int r = 1; r < R; ++r) cm = fmaxf(cm, pm[r]);
+        if (cm > m_w) {  // wave-uniform
+            const float alpha = m_w == -INFINITY ? 0.f : exp_e(m_w - cm);
+            wsum *= alpha;
 #pragma unroll
-                    for (int k = 0; k < DPL; ++k) vals[u][k] = src[k];
-                }
-            }
+            for (int k = 0; k < DPL; ++k) acc[k] *= alpha;
+            m_w = cm;
+        }
+        if (m_w == -INFINITY) continue;  // nothing valid yet (only without valid block ids)
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int idx = i + u * NW;
-                if (idx < n) {
-                    const float wt = exp_e(sm_m[idx] - mx) * sm_e[idx];
-                    wsum += wt;
+        for (int r = 0; r < R; ++r) {
+            if (pm[r] != -INFINITY) {
+                const float wt = exp_e(pm[r] - m_w) * ps[r];
+                wsum += wt;
 #pragma unroll
-                    for (int k = 0; k < DPL; ++k) acc[k] += wt * vals[u][k];
-                }
+                for (int k = 0; k < DPL; ++k) acc[k] += wt * po_v[r][k];
             }
         }
     }
+    if (lane == 0) {
+        sm_m[w] = m_w;
+        sm_w[w] = wsum;
+    }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) sm_acc[w][lane * DPL + k] = acc[k];
-    if (lane == 0) sm_wsum[w] = wsum;
     __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[ww]);
+    float f[NW];
     float total = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) total += sm_wsum[ww];
-    const float inv = 1.f / total;
+    for (int ww = 0; ww < NW; ++ww) {
+        f[ww] = mx == -INFINITY ? 0.f : exp_e(sm_m[ww] - mx);
+        total += f[ww] * sm_w[ww];
+    }
+    // total == 0 only for L == 0 or when no block id of the sequence was valid.
+    const float inv = total > 0.f ? 1.f / total : 0.f;
     for (int d = tid; d < D; d += NT) {
         float o = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) o += sm_acc[ww][d];
+        for (int ww = 0; ww < NW; ++ww) o += f[ww] * sm_acc[ww][d];
         orow[d] = M::from_float(o * inv);
     }
 }
