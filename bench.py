@@ -129,7 +129,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the op shards by "
-              "sequence / kv head / context with no change to the kernels; see DESIGN.md)",
+              "sequence, kv head or context with no change to the kernels)",
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -27,11 +27,17 @@
  *     (paged_attn.py), "Three changes", item 2.
  *
  * Layouts (row-major, contiguous, all in device memory):
- *   query, out      [num_seqs][num_q_heads][head_dim]              dtype
- *   key_cache,
- *   value_cache     [num_blocks][num_kv_heads][block_size][head_dim] dtype
- *   block_tables    [num_seqs][max_blocks_per_seq]                  int32
- *   seq_lens        [num_seqs]                                      int32
+ *   query, out      [num_seqs][num_q_heads][head_dim]                         dtype
+ *   key_cache       [num_blocks][num_kv_heads][head_dim / x][block_size][x]    dtype
+ *   value_cache     [num_blocks][num_kv_heads][head_dim][block_size]           dtype
+ *   block_tables    [num_seqs][max_blocks_per_seq]                             int32
+ *   seq_lens        [num_seqs]                                                 int32
+ * with x = 16 bytes / element size (8 for bf16, 4 for float32): K[t][d] of
+ * slot t of a block is at [..][d / x][t][d % x], V[t][d] at [..][d][t].  The
+ * pages gather whole blocks by id and permute them into token order, leaving
+ * the in-block order open; this is the split layout of paged caches, in
+ * which every 16-byte key group and every value row of a block is contiguous
+ * across its 16 tokens.
  * dtype (PA_DTYPE_F32 or PA_DTYPE_BF16) applies to query, caches and out.
  * Partials in the V2 workspace are always float32 (layout below).
  *

@@ -78,14 +78,15 @@ def _problem(query, key_cache, value_cache, block_tables, seq_lens, dtype):
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
     code, npdt = _DTYPES[dtype]
     _check("query", query, npdt, 3)
-    _check("key_cache", key_cache, npdt, 4)
+    _check("key_cache", key_cache, npdt, 5)
     _check("value_cache", value_cache, npdt, 4)
     _check("block_tables", block_tables, np.int32, 2)
     _check("seq_lens", seq_lens, np.int32, 1)
     S, Hq, D = query.shape
-    _, Hkv, B, D2 = key_cache.shape
-    if key_cache.shape != value_cache.shape or D2 != D:
-        raise ValueError("key/value cache shapes disagree with the query")
+    # keys [blocks][Hkv][D / x][16][x] with x = 16 bytes of values; values [blocks][Hkv][D][16]
+    nb, Hkv, Dx, B, x = key_cache.shape
+    if x * np.dtype(npdt).itemsize != 16 or Dx * x != D or value_cache.shape != (nb, Hkv, D, B):
+        raise ValueError("key/value cache shapes disagree with the query or the split layout")
     if block_tables.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("block_tables / seq_lens rows must equal num_seqs")
     mb = block_tables.shape[1]

@@ -42,9 +42,14 @@
  * the rescale exp(m_p - M) * s_p and the weighted sum of the o_p.
  *
  * Readings where the pages are silent (each also listed in the design notes):
- *   - cache layout [num_blocks][num_kv_heads][block_size][head_dim], query and
- *     output [num_seqs][num_q_heads][head_dim], block table int32
- *     [num_seqs][max_blocks_per_seq] (row-major, contiguous);
+ *   - paged caches in the split layout of the pages' host project (the pages
+ *     gather whole blocks by id and then permute and reshape them into token
+ *     order, which leaves the in-block order open): keys
+ *     [num_blocks][num_kv_heads][head_dim / x][block_size][x] with x = 16 bytes
+ *     / element size (8 bf16 or 4 float32 values), values
+ *     [num_blocks][num_kv_heads][head_dim][block_size]; query and output
+ *     [num_seqs][num_q_heads][head_dim], block table int32
+ *     [num_seqs][max_blocks_per_seq] (all row-major, contiguous);
  *   - the scale multiplies q.k before the max is taken;
  *   - tokens at or beyond L are excluded (never read), not zero-weighted;
  *   - L == 0 gives an all-zero output row;
@@ -84,10 +89,14 @@ typedef struct {
     double scale;
 } problem_t;
 
+/* Values per 16-byte group of the key layout. */
+static int key_group(int dtype) { return dtype == ORACLE_BF16 ? 8 : 4; }
+
 static int check_problem(const problem_t *pb) {
     if (!pb->query || !pb->key_cache || !pb->value_cache || !pb->block_tables || !pb->seq_lens)
         return -1;
     if (pb->dtype != ORACLE_F32 && pb->dtype != ORACLE_BF16) return -2;
+    if (pb->head_dim % key_group(pb->dtype) != 0) return -3;
     if (pb->num_seqs < 0 || pb->num_q_heads <= 0 || pb->num_kv_heads <= 0 || pb->head_dim <= 0 ||
         pb->block_size <= 0 || pb->max_blocks_per_seq < 0)
         return -3;
@@ -95,21 +104,39 @@ static int check_problem(const problem_t *pb) {
     return 0;
 }
 
-/* Offset of element 0 of the key/value row of token t, kv head kvh, sequence s. */
-static size_t kv_row(const problem_t *pb, int s, int kvh, int t) {
+/* (block, kv head) slab index of token t of sequence s, and its slot. */
+static size_t slab_of(const problem_t *pb, int s, int kvh, int t, int *slot) {
     int32_t phys = pb->block_tables[(size_t)s * pb->max_blocks_per_seq + t / pb->block_size];
-    int slot = t % pb->block_size;
-    return (((size_t)phys * pb->num_kv_heads + kvh) * pb->block_size + slot) * pb->head_dim;
+    *slot = t % pb->block_size;
+    return (size_t)phys * pb->num_kv_heads + kvh;
+}
+
+/* Element index of K[t][d] (token t of sequence s, kv head kvh) in the key cache
+ * [num_blocks][num_kv_heads][head_dim / x][block_size][x]. */
+static size_t key_index(const problem_t *pb, int s, int kvh, int t, int d) {
+    int slot;
+    size_t slab = slab_of(pb, s, kvh, t, &slot);
+    int x = key_group(pb->dtype);
+    return ((slab * (size_t)(pb->head_dim / x) + (size_t)(d / x)) * pb->block_size + slot) * x +
+           d % x;
+}
+
+/* Element index of V[t][d] in the value cache
+ * [num_blocks][num_kv_heads][head_dim][block_size]. */
+static size_t value_index(const problem_t *pb, int s, int kvh, int t, int d) {
+    int slot;
+    size_t slab = slab_of(pb, s, kvh, t, &slot);
+    return (slab * (size_t)pb->head_dim + (size_t)d) * pb->block_size + slot;
 }
 
 /* Scaled logit z_t of query head h of sequence s against token t. */
 static double logit(const problem_t *pb, int s, int h, int t) {
     int G = pb->num_q_heads / pb->num_kv_heads;
     size_t qoff = ((size_t)s * pb->num_q_heads + h) * pb->head_dim;
-    size_t koff = kv_row(pb, s, h / G, t);
     double dot = 0.0;
     for (int d = 0; d < pb->head_dim; ++d)
-        dot += elem(pb->query, qoff + d, pb->dtype) * elem(pb->key_cache, koff + d, pb->dtype);
+        dot += elem(pb->query, qoff + d, pb->dtype) *
+               elem(pb->key_cache, key_index(pb, s, h / G, t, d), pb->dtype);
     return pb->scale * dot;
 }
 
@@ -131,9 +158,9 @@ static int attend_range(const problem_t *pb, int s, int h, int t0, int t1, doubl
     double sum = 0.0;
     for (int t = t0; t < t1; ++t) {
         double w = exp(z[t - t0] - zmax);
-        size_t voff = kv_row(pb, s, h / G, t);
         sum += w;
-        for (int d = 0; d < pb->head_dim; ++d) o[d] += w * elem(pb->value_cache, voff + d, pb->dtype);
+        for (int d = 0; d < pb->head_dim; ++d)
+            o[d] += w * elem(pb->value_cache, value_index(pb, s, h / G, t, d), pb->dtype);
     }
     for (int d = 0; d < pb->head_dim; ++d) o[d] /= sum;
     free(z);

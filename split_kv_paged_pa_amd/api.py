@@ -113,17 +113,26 @@ def _dev(name, t, dtype=None, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def key_group(dtype: torch.dtype) -> int:
+    """x of the key layout: values per 16-byte group (8 for bf16, 4 for float32)."""
+    return 16 // torch.empty((), dtype=dtype).element_size()
+
+
 def _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len):
     if query.dtype not in _DTYPE_CODE:
         raise TypeError(f"query dtype must be float32 or bfloat16, got {query.dtype}")
+    if query.dim() != 3 or key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("query [S, Hq, D], key_cache [blocks, Hkv, D/x, 16, x] and "
+                         "value_cache [blocks, Hkv, D, 16] expected")
     S, Hq, D = query.shape
-    nb, Hkv, B, D2 = key_cache.shape
-    if value_cache.shape != key_cache.shape or D2 != D:
-        raise ValueError("key_cache / value_cache / query shapes disagree")
+    nb, Hkv, Dx, B, x = key_cache.shape
+    if x != key_group(query.dtype) or Dx * x != D or tuple(value_cache.shape) != (nb, Hkv, D, B):
+        raise ValueError(f"cache shapes {tuple(key_cache.shape)} / {tuple(value_cache.shape)} do "
+                         f"not match the query {tuple(query.shape)} in the split layout")
     if block_tables.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("block_tables and seq_lens need one row per sequence")
     args = [_dev("query", query, None, 3),
-            _dev("key_cache", key_cache, query.dtype, 4),
+            _dev("key_cache", key_cache, query.dtype, 5),
             _dev("value_cache", value_cache, query.dtype, 4),
             _dev("block_tables", block_tables, torch.int32, 2),
             _dev("seq_lens", seq_lens, torch.int32, 1),

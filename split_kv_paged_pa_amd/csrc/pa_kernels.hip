@@ -21,18 +21,18 @@
 //     query heads of the group sit in the N dimension of one 16x16 MFMA tile,
 //     so every key/value block is read from HBM once for the whole group.
 //   - A wave owns whole 16-token blocks (blocks j = first + w, first + w + NW, ...).
-//     Lane l loads 16 bytes of token (l % 16), at byte 64*c + 16*(l / 16) of the
-//     row, for c = 0 .. NC-1: four dwordx4 loads per lane cover a 4 KiB bf16
-//     D=128 block, every 64-byte segment fully used.
+//     The caches use the split layout (keys [D/x][16][x], values [D][16] per
+//     block and kv head, x = 16 bytes of values), so every load instruction of
+//     a wave reads contiguous memory: key chunk c of lane l is the 16 bytes at
+//     1024*c + 16*l of the slab (token l % 16, d group 4c + l / 16), and value
+//     tile T of lane (i, grp) is the 4 tokens 4*grp .. 4*grp+3 of row d = 16T + i.
 //   - QK^T: MFMA with A = keys (rows = tokens), B = Q^T (cols = heads).  The
 //     result tile holds, in lane (g, grp) register i, the logit of token
 //     4*grp + i for head g -- exactly the B-operand layout P^T needs for PV,
 //     so the softmax weights never leave their lane.
-//   - V is read row-major (tokens x d), but PV reduces over tokens, which MFMA
-//     wants contiguous per lane.  The transpose is done in registers by one
-//     MFMA against a 0/1 selection matrix (exact: each output is one value
-//     times 1 plus zeros); the result is the A operand of O^T = V^T P^T.
-//     No LDS traffic in the block loop.
+//   - PV as O^T = V^T P^T: the value registers as loaded are the A operand (row
+//     d, four consecutive tokens per lane), so no transpose is needed and the
+//     block loop touches no LDS.
 //   - Masked tokens (past the sequence end) get logit -inf and their value
 //     registers are zeroed before any MFMA touches them, so stale or NaN cache
 //     slots cannot leak through 0 * NaN.
@@ -99,16 +99,18 @@ __device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s1
 __device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
 
 // ---------------------------------------------------------------------------
-// Element-type specific MFMA steps.  For both types a lane works on "chunk c":
-// the 16 bytes at byte 64*c + 16*grp of a row (grp = lane / 16), i.e. E
-// consecutive d values starting at d = c*4E + grp*E.
+// Element-type specific MFMA steps.
+//   Keys: a lane holds "chunk c" of its token row: E consecutive d values
+//   starting at d = (4c + grp) * E (grp = lane / 16), i.e. 16 bytes.
+//   Values: a lane (i, grp) holds, for d tile T, the four tokens 4*grp .. 4*grp+3
+//   of dimension d = 16T + i (one VU).
 // ---------------------------------------------------------------------------
 template <typename T> struct Mma;
 
 // bf16 storage (uint16 bit patterns): v_mfma_f32_16x16x16_bf16, 4 values per lane.
 template <> struct Mma<uint16_t> {
-    static constexpr int E = 8;        // elements per 16-byte chunk
-    static constexpr int kTiles = 2;   // f32x4 accumulator tiles per chunk
+    static constexpr int E = 8;  // elements per 16-byte key chunk
+    typedef u32x2 VU;            // four bf16 tokens of one d
 
     // S[t][g] += sum over the chunk's d of K[t][d] Q[g][d].
     static __device__ __forceinline__ void qk(f32x4 &s, uint4 k, uint4 q) {
@@ -116,27 +118,22 @@ template <> struct Mma<uint16_t> {
         s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi_half(k), hi_half(q), s, 0, 0, 0);
     }
 
-    struct Consts { s16x4 ident; };
-    static __device__ __forceinline__ Consts consts(int l16, int grp) {
-        float e[4];
-        for (int i = 0; i < 4; ++i) e[i] = (4 * grp + i == l16) ? 1.f : 0.f;
-        return {pack_bf16(e[0], e[1], e[2], e[3])};
-    }
-
     struct Probs { s16x4 p; };
     static __device__ __forceinline__ Probs probs(const float *p) {
         return {pack_bf16(p[0], p[1], p[2], p[3])};
     }
 
-    // acc[h] (lane (g, grp), register r) += sum_t P[g][t] V[t][c*32 + grp*8 + 4h + r].
-    static __device__ __forceinline__ void pv(f32x4 *acc, uint4 v, const Consts &k, const Probs &pr) {
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        // Transpose: T[t][j] = V[t][d(j)], lane (j, grp) register r = token 4*grp + r.
-        f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo_half(v), k.ident, zero, 0, 0, 0);
-        f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi_half(v), k.ident, zero, 0, 0, 0);
-        // t0/t1 hold bf16 values exactly, so the conversion back is exact.
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16(t0), pr.p, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16(t1), pr.p, acc[1], 0, 0, 0);
+    // acc (lane (g, grp), register r) += sum_t V[16T + 4*grp + r][t] P[g][t]:
+    // O^T = V^T P^T, with v already in the A-operand layout (row d, 4 tokens).
+    static __device__ __forceinline__ void pv(f32x4 &acc, VU v, const Probs &pr) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pr.p, acc, 0, 0, 0);
+    }
+
+    // Zero the tokens 4*grp + e >= valid of v (e = 0..3).
+    static __device__ __forceinline__ VU mask(VU v, int keep) {
+        const uint32_t m0 = keep >= 2 ? 0xffffffffu : (keep == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m1 = keep >= 4 ? 0xffffffffu : (keep == 3 ? 0x0000ffffu : 0u);
+        return VU{v[0] & m0, v[1] & m1};
     }
 
     static __device__ __forceinline__ float to_float(uint16_t x) {
@@ -150,7 +147,7 @@ template <> struct Mma<uint16_t> {
 // float32 storage: v_mfma_f32_16x16x4_f32, one value per lane per MFMA.
 template <> struct Mma<float> {
     static constexpr int E = 4;
-    static constexpr int kTiles = 1;
+    typedef uint4 VU;  // four fp32 tokens of one d
 
     static __device__ __forceinline__ void qk(f32x4 &s, uint4 k, uint4 q) {
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), s, 0, 0, 0);
@@ -159,28 +156,21 @@ template <> struct Mma<float> {
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), __uint_as_float(q.w), s, 0, 0, 0);
     }
 
-    // sel[e] in lane (j, grp) is 1 iff j == 4*grp + e.
-    struct Consts { float sel[4]; };
-    static __device__ __forceinline__ Consts consts(int l16, int grp) {
-        Consts c;
-        for (int e = 0; e < 4; ++e) c.sel[e] = (l16 == 4 * grp + e) ? 1.f : 0.f;
-        return c;
-    }
-
     struct Probs { float p[4]; };
     static __device__ __forceinline__ Probs probs(const float *p) { return {{p[0], p[1], p[2], p[3]}}; }
 
-    // acc[0] (lane (g, grp), register r) += sum_t P[g][t] V[t][c*16 + grp*4 + r].
-    static __device__ __forceinline__ void pv(f32x4 *acc, uint4 v, const Consts &k, const Probs &pr) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-        // Transpose: T[t][j] = V[t][c*16 + j]; lane (j, grp) register r = token 4*grp + r.
-        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), k.sel[0], t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), k.sel[1], t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), k.sel[2], t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), k.sel[3], t, 0, 0, 0);
-        // Token 4*k + r of the block is the MFMA-r reduction index k.
-        for (int r = 0; r < 4; ++r)
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(t[r], pr.p[r], acc[0], 0, 0, 0);
+    // MFMA m reduces over the tokens 4*grp + m: lane (i, grp) gives V[d][4*grp + m]
+    // (component m of v), lane (g, grp) gives P[g][4*grp + m] (register m of P^T).
+    static __device__ __forceinline__ void pv(f32x4 &acc, VU v, const Probs &pr) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), pr.p[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), pr.p[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), pr.p[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), pr.p[3], acc, 0, 0, 0);
+    }
+
+    static __device__ __forceinline__ VU mask(VU v, int keep) {
+        return make_uint4(keep > 0 ? v.x : 0u, keep > 1 ? v.y : 0u, keep > 2 ? v.z : 0u,
+                          keep > 3 ? v.w : 0u);
     }
 
     static __device__ __forceinline__ float to_float(float x) { return x; }
@@ -203,9 +193,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     float *__restrict__ exp_sums, float *__restrict__ max_logits, T *__restrict__ out) {
     using M = Mma<T>;
     constexpr int E = M::E;
-    constexpr int NC = D / (4 * E);          // 16-byte chunks per lane per row
-    constexpr int ROW16 = D / E;             // 16-byte units per row
-    constexpr int NT = NC * M::kTiles;       // accumulator tiles per lane
+    using VU = typename M::VU;
+    constexpr int NC = D / (4 * E);          // key chunks (16 bytes) per lane per block
+    constexpr int NT = D / 16;               // d tiles: value units and accumulator tiles
     constexpr int LDS_STRIDE = D + 4;
 
     __shared__ float sm_m[NW][16];
@@ -252,7 +242,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c) qv[c] = make_uint4(0, 0, 0, 0);
     }
-    const typename M::Consts kc = M::consts(l16, grp);
 
     float m_run = -INFINITY;  // running max logit of column g
     float l_run = 0.f;        // this lane's share of the running exp-sum
@@ -262,8 +251,17 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
     const size_t slab = (size_t)kBlockTokens * D;        // elements of one (block, kv head) slab
-    const size_t lane_off = (size_t)l16 * ROW16 + grp;  // this lane's first uint4 in a slab
-    const uint4 *dummy = reinterpret_cast<const uint4 *>(
+    // Byte offsets inside a (block, kv head) slab.  Keys, [D/E][16][E]: chunk c of
+    // lane l is the 16 bytes at 1024*c + 16*l, so each load instruction reads 1 KiB
+    // of contiguous memory.  Values, [D][16]: tile T of lane (i, grp) is the
+    // 4 tokens at row d = 16T + i, byte 4*grp*sizeof(T); one instruction reads the
+    // contiguous 16 rows of a tile.
+    constexpr int kRowBytes = kBlockTokens * (int)sizeof(T);  // one value row (d)
+    constexpr int kKStep = 1024;
+    constexpr int kVStep = 16 * kRowBytes;
+    const int k_lane = 16 * lane;
+    const int v_lane = kRowBytes * l16 + 4 * (int)sizeof(T) * grp;
+    const char *dummy = reinterpret_cast<const char *>(
         query + ((size_t)s * num_q_heads + (size_t)kvh * group) * D);
 
     // ---- issue side: wave w takes blocks p*bp + w, p*bp + w + NW, ... of each of
@@ -285,7 +283,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     // a block id outside [0, num_blocks), they read the (cached) query row and the
     // block is not attended -- so the compiler keeps exactly the younger ring
     // slots outstanding at each wait.
-    auto issue = [&](uint4 (&kr)[NC], uint4 (&vr)[NC], int &part, int &blk) -> bool {
+    auto issue = [&](uint4 (&kr)[NC], VU (&vr)[NT], int &part, int &blk) -> bool {
         part = i_p;
         blk = i_j;
         const int phys = id_next;
@@ -295,19 +293,22 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             settle();
             id_next = i_p < p_end ? bt[i_j] : 0;
         }
+        // A dummy issue reads the same 16 bytes of the query row in every load.
         const size_t base = ok ? ((size_t)phys * num_kv_heads + kvh) * slab : 0;
-        const uint4 *kp = ok ? reinterpret_cast<const uint4 *>(key_cache + base) + lane_off : dummy;
-        const uint4 *vp = ok ? reinterpret_cast<const uint4 *>(value_cache + base) + lane_off : dummy;
+        const char *kp = ok ? reinterpret_cast<const char *>(key_cache + base) + k_lane : dummy;
+        const char *vp = ok ? reinterpret_cast<const char *>(value_cache + base) + v_lane : dummy;
+        const int ks = ok ? kKStep : 0;
+        const int vs = ok ? kVStep : 0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) kr[c] = kp[c * 4];
+        for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kp + c * ks);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) vr[c] = vp[c * 4];
+        for (int t = 0; t < NT; ++t) vr[t] = *reinterpret_cast<const VU *>(vp + t * vs);
         return ok;
     };
 
     // One block: logits, running-max update, weights, PV.  kTail: the block
     // holds the end of the sequence, so some of its slots are masked.
-    auto attend = [&](auto tail, int j, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+    auto attend = [&](auto tail, int j, const uint4 (&kr)[NC], VU (&vr)[NT]) {
         constexpr bool kTail = decltype(tail)::value;
         const int valid = L - j * kBlockTokens;  // tokens of the block in range (>= 1)
         // Two independent MFMA chains (even / odd chunks) halve the dependent latency.
@@ -339,15 +340,16 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         for (int r = 0; r < 4; ++r) pr[r] = exp_e(z[r] - m_run);
         l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-        if (kTail && l16 >= valid) {
+        if (kTail) {
+            const int keep = valid - 4 * grp;  // tokens of this lane's four still in range
 #pragma unroll
-            for (int c = 0; c < NC; ++c) vr[c] = make_uint4(0, 0, 0, 0);
+            for (int t = 0; t < NT; ++t) vr[t] = M::mask(vr[t], keep);
         }
         const typename M::Probs pb = M::probs(pr);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) M::pv(&acc[c * M::kTiles], vr[c], kc, pb);
+        for (int t = 0; t < NT; ++t) M::pv(acc[t], vr[t], pb);
     };
-    auto step = [&](int j, const uint4 (&kr)[NC], uint4 (&vr)[NC]) {
+    auto step = [&](int j, const uint4 (&kr)[NC], VU (&vr)[NT]) {
         if ((j + 1) * kBlockTokens <= L)
             attend(std::false_type{}, j, kr, vr);
         else
@@ -358,19 +360,14 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     auto finish = [&](int p) {
         const float l_col = column_sum(l_run);
         __syncthreads();  // the previous partition's readers are done with the LDS
-        // lane (g, grp) owns d = c*4E + grp*E + [0, E).
+        // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of head g.
         if (grp == 0) {
             sm_m[w][g] = m_run;
             sm_l[w][g] = l_col;
         }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int t = 0; t < M::kTiles; ++t) {
-                float *dst = &sm_o[w][g][c * 4 * E + grp * E + t * 4];
-                *reinterpret_cast<f32x4 *>(dst) = acc[c * M::kTiles + t];
-            }
-        }
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4 *>(&sm_o[w][g][16 * t + 4 * grp]) = acc[t];
         __syncthreads();
         const size_t head0 = (size_t)s * num_q_heads + (size_t)kvh * group;
         // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
@@ -418,7 +415,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     // next block belongs to a later one.  Every wave closes every partition once,
     // so the barriers inside finish() line up across the waves.
     int a_p = p_begin;
-    uint4 kb[U][NC], vb[U][NC];
+    uint4 kb[U][NC];
+    VU vb[U][NT];
     int sp[U], sj[U];
     bool live[U];
 #pragma unroll

@@ -13,8 +13,8 @@ enum class Dtype : int { F32 = 0, BF16 = 1 };
 // One decode batch, already validated by the ABI layer.
 struct Problem {
     const void *query;          // [S][Hq][D]
-    const void *key_cache;      // [num_blocks][Hkv][16][D]
-    const void *value_cache;    // [num_blocks][Hkv][16][D]
+    const void *key_cache;      // [num_blocks][Hkv][D / x][16][x], x = 16 bytes of values
+    const void *value_cache;    // [num_blocks][Hkv][D][16]
     const int32_t *block_tables;  // [S][max_blocks]
     const int32_t *seq_lens;    // [S]
     int num_seqs, num_q_heads, num_kv_heads, head_dim;

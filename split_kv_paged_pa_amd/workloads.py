@@ -20,6 +20,13 @@ Recipe (every draw is reproducible from (config seed, stream, chunk)):
   - poison (default on): unused pool blocks and the slots past the end of each
     sequence's last block are NaN, so any read of them shows up in the output.
 
+Cache layout (the split layout of paged caches): keys
+[num_blocks][num_kv_heads][head_dim / x][16][x] with x = 16 bytes of values
+(8 bf16, 4 float32), values [num_blocks][num_kv_heads][head_dim][16].  The
+random draws are made per token row ([block][kv head][slot][d], "logical"
+order) and then stored in that layout; pack_kv / unpack_kv convert between the
+two orders.
+
 Streams: query 0, keys 1, values 2, block permutation 3, sequence lengths 4,
 outlier rows 5, length order 6.
 """
@@ -82,6 +89,42 @@ class Spec:
             self.elem_size * 2
 
 
+def key_group(elem_size: int) -> int:
+    """Values per 16-byte group of the key layout."""
+    return 16 // elem_size
+
+
+def _swap(a, i, j):
+    return a.transpose(i, j) if isinstance(a, torch.Tensor) else a.swapaxes(i, j)
+
+
+def pack_kv(k, v, elem_size: int | None = None):
+    """Logical [num_blocks, Hkv, 16, D] keys and values (numpy or torch, bf16 as
+    uint16 in numpy) -> contiguous caches in the split layout:
+    keys [num_blocks, Hkv, D / x, 16, x], values [num_blocks, Hkv, D, 16].
+    x follows the arrays' element size unless elem_size (of the dtype the
+    caches will be stored in) is given."""
+    nb, H, B, D = k.shape
+    if elem_size is None:
+        elem_size = k.element_size() if isinstance(k, torch.Tensor) else k.itemsize
+    x = key_group(elem_size)
+    kc = _swap(k.reshape(nb, H, B, D // x, x), 2, 3)
+    vc = _swap(v, 2, 3)
+    if isinstance(k, torch.Tensor):
+        return kc.contiguous(), vc.contiguous()
+    return np.ascontiguousarray(kc), np.ascontiguousarray(vc)
+
+
+def unpack_kv(kc, vc):
+    """Inverse of pack_kv: logical [num_blocks, Hkv, 16, D] copies."""
+    nb, H, Dx, B, x = kc.shape
+    k = _swap(kc, 2, 3).reshape(nb, H, B, Dx * x)
+    v = _swap(vc, 2, 3)
+    if isinstance(kc, torch.Tensor):
+        return k.contiguous(), v.contiguous()
+    return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
 def _inv_sqrt(d: int) -> float:
     return float(np.float32(1.0 / math.sqrt(d)))
 
@@ -140,8 +183,8 @@ class Batch:
     """A generated batch: torch CPU tensors in the paged layout."""
     spec: Spec
     query: torch.Tensor          # [S, Hq, D]
-    key_cache: torch.Tensor      # [num_blocks, Hkv, 16, D]
-    value_cache: torch.Tensor    # [num_blocks, Hkv, 16, D]
+    key_cache: torch.Tensor      # [num_blocks, Hkv, D / x, 16, x]
+    value_cache: torch.Tensor    # [num_blocks, Hkv, D, 16]
     block_tables: torch.Tensor   # int32 [S, max_blocks_per_seq]
     seq_lens: torch.Tensor       # int32 [S]
     extras: dict = field(default_factory=dict)
@@ -151,6 +194,12 @@ class Batch:
         bf16 tensors come out as uint16 bit patterns."""
         return (to_numpy(self.query), to_numpy(self.key_cache), to_numpy(self.value_cache),
                 self.block_tables.numpy(), self.seq_lens.numpy())
+
+    def numpy_logical(self):
+        """As numpy(), but keys and values as logical [num_blocks, Hkv, 16, D] copies."""
+        q, kc, vc, bt, sl = self.numpy()
+        k, v = unpack_kv(kc, vc)
+        return q, k, v, bt, sl
 
 
 def torch_dtype(dtype: str) -> torch.dtype:
@@ -193,8 +242,9 @@ def generate(spec: Spec, poison: bool = True, threads: int | None = None) -> Bat
     query = torch.from_numpy(q).to(tdt)
 
     fill = float("nan") if poison else 0.0
-    kc = torch.full((spec.num_blocks, Hkv, BLOCK_SIZE, D), fill, dtype=tdt)
-    vc = torch.full((spec.num_blocks, Hkv, BLOCK_SIZE, D), fill, dtype=tdt)
+    x = key_group(spec.elem_size)
+    kc = torch.full((spec.num_blocks, Hkv, D // x, BLOCK_SIZE, x), fill, dtype=tdt)
+    vc = torch.full((spec.num_blocks, Hkv, D, BLOCK_SIZE), fill, dtype=tdt)
     perm_t = torch.from_numpy(perm.astype(np.int64))
 
     def fill_chunk(ci: int):
@@ -207,8 +257,9 @@ def generate(spec: Spec, poison: bool = True, threads: int | None = None) -> Bat
             rows = _rng(spec.seed, _STREAM_OUTLIER, ci).random((n, Hkv, BLOCK_SIZE)) < spec.outlier_frac
             k[rows] *= np.float32(spec.outlier_mult)
         idx = perm_t[b0:b1]
-        kc[idx] = torch.from_numpy(k).to(tdt)
-        vc[idx] = torch.from_numpy(v).to(tdt)
+        ks, vs = pack_kv(k, v, spec.elem_size)
+        kc[idx] = torch.from_numpy(ks).to(tdt)
+        vc[idx] = torch.from_numpy(vs).to(tdt)
 
     nchunks = -(-total // _CHUNK_BLOCKS)
     with ThreadPoolExecutor(threads or _workers()) as ex:
@@ -219,8 +270,8 @@ def generate(spec: Spec, poison: bool = True, threads: int | None = None) -> Bat
             r = int(lens[s] % BLOCK_SIZE)
             if r:
                 last = int(tables[s, nblk[s] - 1])
-                kc[last, :, r:, :] = float("nan")
-                vc[last, :, r:, :] = float("nan")
+                kc[last, :, :, r:, :] = float("nan")
+                vc[last, :, :, r:] = float("nan")
 
     return Batch(spec, query, kc, vc, torch.from_numpy(tables),
                  torch.from_numpy(spec.seq_lens.astype(np.int32).copy()))

@@ -27,7 +27,8 @@ def widen(a):
 
 
 def dense_kv(kc, vc, bt, L, s):
-    """Dense [Hkv, L, D] keys/values of sequence s, gathered with numpy fancy indexing."""
+    """Dense [Hkv, L, D] keys/values of sequence s, gathered with numpy fancy indexing
+    from logical [blocks, Hkv, 16, D] keys and values."""
     nblk = -(-L // wl.BLOCK_SIZE)
     blocks = bt[s, :nblk]
     k = widen(kc[blocks]).transpose(1, 0, 2, 3).reshape(kc.shape[1], nblk * wl.BLOCK_SIZE, -1)
@@ -36,7 +37,8 @@ def dense_kv(kc, vc, bt, L, s):
 
 
 def sdpa_reference(q, kc, vc, bt, sl, scale):
-    """Dense attention through torch's scaled_dot_product_attention in float64."""
+    """Dense attention through torch's scaled_dot_product_attention in float64
+    (logical [blocks, Hkv, 16, D] keys and values)."""
     S, Hq, D = q.shape
     Hkv = kc.shape[1]
     G = Hq // Hkv
@@ -61,12 +63,19 @@ def _run(batch, lib=None, **kw):
     return oracle.decode(q, kc, vc, bt, sl, batch.spec.scale, dtype=batch.spec.dtype, lib=lib, **kw)
 
 
+def _decode(q, k, v, bt, sl, spec, lib=None):
+    """The oracle on logical [blocks, Hkv, 16, D] keys and values, stored into the
+    cache layout by the generator's pack_kv first."""
+    kc, vc = wl.pack_kv(k, v)
+    return oracle.decode(q, kc, vc, bt, sl, spec.scale, dtype=spec.dtype, lib=lib)
+
+
 def pin_single_token(lib=None):
     """L = 1: the softmax has one term, so the output is that token's value row exactly."""
     for dtype in ("f32", "bf16"):
         spec = wl.custom("one", 11, dtype, 6, 2, 64, [1, 1, 1], num_blocks=9)
         b = wl.generate(spec)
-        q, kc, vc, bt, sl = b.numpy()
+        q, kc, vc, bt, sl = b.numpy_logical()
         out = _run(b, lib)
         for s in range(3):
             for h in range(6):
@@ -80,12 +89,13 @@ def pin_uniform_keys(lib=None):
     for zero_q in (False, True):
         spec = wl.custom("uniform", 12, "bf16", 8, 2, 64, [37, 16, 300], num_blocks=40)
         b = wl.generate(spec)
-        q, kc, vc, bt, sl = b.numpy()
+        q, kc, vc, bt, sl = b.numpy_logical()
+        q = q.copy()
         if zero_q:
             q[:] = 0
         else:
             kc[np.isfinite(widen(kc))] = kc[bt[0, 0], 0, 0, 0]  # one bf16 value everywhere finite
-        out = _run(b, lib)
+        out = _decode(q, kc, vc, bt, sl, spec, lib)
         for s in range(3):
             L = int(sl[s])
             _, v = dense_kv(kc, vc, bt, L, s)
@@ -101,14 +111,14 @@ def pin_positional_values(lib=None):
     lens = [1, 15, 16, 17, 100, 333]
     spec = wl.custom("positional", 13, "f32", 4, 4, 64, lens, num_blocks=64)
     b = wl.generate(spec)
-    q, kc, vc, bt, sl = b.numpy()
+    q, kc, vc, bt, sl = b.numpy_logical()
     for s, L in enumerate(lens):
         for t in range(L):
             blk, r = bt[s, t // 16], t % 16
             kc[blk, :, r, :] = 0.5
             vc[blk, :, r, :] = 0.0
             vc[blk, :, r, 0] = float(t)
-    out = _run(b, lib)
+    out = _decode(q, kc, vc, bt, sl, spec, lib)
     for s, L in enumerate(lens):
         assert np.all(out[s, :, 0] == (L - 1) / 2), f"positional mean, L={L}"
         assert np.all(out[s, :, 1:] == 0.0), f"positional rest, L={L}"
@@ -121,7 +131,8 @@ def pin_closed_form(lib=None):
     D = g["head_dim"]
     spec = wl.custom("closed", 14, "f32", 1, 1, D, [2], num_blocks=2, scale=g["scale"])
     b = wl.generate(spec)
-    q, kc, vc, bt, sl = b.numpy()
+    q, kc, vc, bt, sl = b.numpy_logical()
+    q = q.copy()
     q[:] = 0
     q[0, 0, 0] = 1.0
     blk = bt[0, 0]
@@ -131,7 +142,7 @@ def pin_closed_form(lib=None):
     vc[blk, 0, :2, :] = 0
     vc[blk, 0, 0, 0] = 4.0
     vc[blk, 0, 1, 1] = 4.0
-    out = _run(b, lib)[0, 0]
+    out = _decode(q, kc, vc, bt, sl, spec, lib)[0, 0]
     expect = np.zeros(D)
     expect[0] = g["expected_out"]["0"]
     expect[1] = g["expected_out"]["1"]
@@ -142,13 +153,13 @@ def pin_head_mapping(lib=None):
     """Values of kv head k all equal k + 1: query head h must return h // G + 1."""
     spec = wl.custom("heads", 15, "bf16", 12, 3, 64, [50, 7], num_blocks=16)
     b = wl.generate(spec)
-    q, kc, vc, bt, sl = b.numpy()
+    q, kc, vc, bt, sl = b.numpy_logical()
     vals = widen(vc)
     for k in range(3):
         fin = np.isfinite(vals[:, k])
         sub = vc[:, k]
         sub[fin] = np.array([k + 1], np.float32).view(np.uint32)[0] >> 16
-    out = _run(b, lib)
+    out = _decode(q, kc, vc, bt, sl, spec, lib)
     for h in range(12):
         assert np.max(np.abs(out[:, h, :] - (h // 4 + 1))) <= 1e-14, f"head mapping h={h}"
 
@@ -158,7 +169,7 @@ def pin_dense_library(lib=None):
     for dtype, D, Hq, Hkv in (("f32", 64, 8, 2), ("bf16", 128, 10, 2), ("bf16", 64, 4, 4)):
         spec = wl.custom("dense", 16, dtype, Hq, Hkv, D, [1, 15, 16, 17, 250, 513, 0], num_blocks=80)
         b = wl.generate(spec)
-        q, kc, vc, bt, sl = b.numpy()
+        q, kc, vc, bt, sl = b.numpy_logical()
         out = _run(b, lib)
         ref = sdpa_reference(q, kc, vc, bt, sl, spec.scale)
         assert np.all(np.isfinite(out)), "non-finite output"
@@ -171,7 +182,7 @@ def pin_outlier_stability(lib=None):
     spec = wl.custom("outliers", 17, "bf16", 8, 1, 128, [700, 65], num_blocks=60,
                      outlier_frac=0.05, outlier_mult=40.0)
     b = wl.generate(spec)
-    q, kc, vc, bt, sl = b.numpy()
+    q, kc, vc, bt, sl = b.numpy_logical()
     qw = widen(q)
     top = max(float(np.max(dense_kv(kc, vc, bt, int(sl[s]), s)[0][0] @ qw[s].T)) for s in range(2))
     assert top * spec.scale > math.log(np.finfo(np.float32).max), "test input too mild"
@@ -230,7 +241,8 @@ def pin_partition_statistics(lib=None):
     q, kc, vc, bt, sl = b.numpy()
     P = 256
     tmp, es, ml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P, dtype="f32", lib=lib)
-    k, v = dense_kv(kc, vc, bt, 700, 0)
+    _, kl, vl, _, _ = b.numpy_logical()
+    k, v = dense_kv(kl, vl, bt, 700, 0)
     qw = widen(q)[0]
     sc = float(np.float32(spec.scale))
     for h in range(4):
@@ -253,13 +265,14 @@ def pin_page_counts(lib=None):
     spec = wl.custom("pagecounts", 21, "bf16", 1, 1, 64, [L], num_blocks=g["blocks"])
     b = wl.generate(spec, poison=True)
     q, kc, vc, bt, sl = b.numpy()
+    _, kl, vl, _, _ = b.numpy_logical()
     assert int(np.sum(bt >= 0)) == g["blocks"]
     for P, n in g["partitions"].items():
         tmp, es, ml = oracle.partials(q, kc, vc, bt, sl, spec.scale, int(P), dtype="bf16",
                                       max_partitions=n + 2, lib=lib)
         assert int(np.sum(np.isfinite(ml[0, 0]))) == n, f"P={P}"
         last = g["last_partition_tokens"][P]
-        k, v = dense_kv(kc, vc, bt, L, 0)
+        k, v = dense_kv(kl, vl, bt, L, 0)
         z = float(np.float32(spec.scale)) * (k[0][-last:] @ widen(q)[0, 0])
         assert abs(ml[0, 0, n - 1] - z.max()) <= 1e-12, f"last partition of P={P}"
 

@@ -121,7 +121,21 @@ def test_empty_batch_is_a_no_op():
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 8, 64)
-    kc = torch.zeros(4, 2, 16, 64)
+    kc = torch.zeros(4, 2, 16, 16, 4)
+    vc = torch.zeros(4, 2, 64, 16)
     with pytest.raises(ValueError, match="GPU"):
-        pa.pa_decode_v1(torch.zeros_like(q), q, kc, kc, torch.zeros(1, 4, dtype=torch.int32),
+        pa.pa_decode_v1(torch.zeros_like(q), q, kc, vc, torch.zeros(1, 4, dtype=torch.int32),
+                        torch.ones(1, dtype=torch.int32), 0.125, 1)
+
+
+def test_binding_checks_the_split_layout():
+    import torch
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 2, 16, 16, 4, dtype=torch.bfloat16)  # x = 4 is the float32 grouping
+    vc = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="split layout"):
+        pa.pa_decode_v1(torch.zeros_like(q), q, kc, vc, torch.zeros(1, 4, dtype=torch.int32),
+                        torch.ones(1, dtype=torch.int32), 0.125, 1)
+    with pytest.raises(ValueError, match="expected"):
+        pa.pa_decode_v1(torch.zeros_like(q), q, vc, vc, torch.zeros(1, 4, dtype=torch.int32),
                         torch.ones(1, dtype=torch.int32), 0.125, 1)

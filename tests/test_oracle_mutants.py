@@ -18,16 +18,23 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 # (name, text in pa_oracle.c, replacement)
 MUTANTS = [
-    ("gqa_modulo_map", "size_t koff = kv_row(pb, s, h / G, t);",
-     "size_t koff = kv_row(pb, s, h % pb->num_kv_heads, t);"),
-    ("value_head_map", "size_t voff = kv_row(pb, s, h / G, t);",
-     "size_t voff = kv_row(pb, s, h % pb->num_kv_heads, t);"),
+    ("gqa_modulo_map", "elem(pb->key_cache, key_index(pb, s, h / G, t, d), pb->dtype);",
+     "elem(pb->key_cache, key_index(pb, s, h % pb->num_kv_heads, t, d), pb->dtype);"),
+    ("value_head_map", "elem(pb->value_cache, value_index(pb, s, h / G, t, d), pb->dtype);",
+     "elem(pb->value_cache, value_index(pb, s, h % pb->num_kv_heads, t, d), pb->dtype);"),
     ("logical_not_physical_block",
      "int32_t phys = pb->block_tables[(size_t)s * pb->max_blocks_per_seq + t / pb->block_size];",
      "int32_t phys = t / pb->block_size; (void)s;"),
-    ("slot_axis_swapped",
-     "return (((size_t)phys * pb->num_kv_heads + kvh) * pb->block_size + slot) * pb->head_dim;",
-     "return (((size_t)phys * pb->block_size + slot) * pb->num_kv_heads + kvh) * pb->head_dim;"),
+    ("slab_axes_swapped", "return (size_t)phys * pb->num_kv_heads + kvh;",
+     "return (size_t)kvh * pb->num_kv_heads + phys;"),
+    ("key_layout_unsplit",
+     "return ((slab * (size_t)(pb->head_dim / x) + (size_t)(d / x)) * pb->block_size + slot) * x +\n"
+     "           d % x;",
+     "return (slab * pb->block_size + slot) * (size_t)pb->head_dim + d + 0 * x;"),
+    ("key_group_fixed", "return dtype == ORACLE_BF16 ? 8 : 4;", "return 8 + 0 * dtype;"),
+    ("value_layout_token_major",
+     "return (slab * (size_t)pb->head_dim + (size_t)d) * pb->block_size + slot;",
+     "return (slab * pb->block_size + slot) * (size_t)pb->head_dim + d;"),
     ("scale_dropped", "return pb->scale * dot;", "return dot;"),
     ("scale_squared", "return pb->scale * dot;", "return pb->scale * pb->scale * dot;"),
     ("tail_not_masked", "if (attend_range(&pb, s, h, 0, L, o, &m, &den)) {",

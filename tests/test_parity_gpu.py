@@ -148,7 +148,7 @@ def test_out_of_range_block_ids_are_skipped():
     db.block_tables = bt.to("cuda")
     # Reference: the same sequences with those blocks' tokens zero-weighted, i.e. the
     # oracle over a copy whose removed tokens carry logit -inf: rebuild without them.
-    q, kc, vc, bt_np, _ = b.numpy()
+    q, kc, vc, bt_np, _ = b.numpy_logical()
     keep0 = [j for j in range(7) if j != 2]
     keep1 = [1, 2, 3]
     rows = []
@@ -163,7 +163,7 @@ def test_out_of_range_block_ids_are_skipped():
         for i in range(n):
             kk[i // 16, :, i % 16] = dense_k[i]
             vv[i // 16, :, i % 16] = dense_v[i]
-        ref = oracle.decode(np.ascontiguousarray(q[s:s + 1]), kk, vv,
+        ref = oracle.decode(np.ascontiguousarray(q[s:s + 1]), *wl.pack_kv(kk, vv),
                             np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
                             spec.scale, dtype="f32")
         rows.append(ref[0])

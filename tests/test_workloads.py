@@ -17,7 +17,7 @@ def test_same_seed_same_bytes_any_thread_count():
 def test_poison_layout():
     spec = wl.custom("poison", 6, "f32", 4, 2, 64, [33, 16, 1], num_blocks=12)
     b = wl.generate(spec)
-    q, kc, vc, bt, sl = b.numpy()
+    q, kc, vc, bt, sl = b.numpy_logical()
     used = set()
     for s, L in enumerate(sl):
         nblk = -(-int(L) // 16)
@@ -57,7 +57,31 @@ def test_named_configs():
 
 def test_tiny_config_generates():
     b = wl.generate(wl.config("tiny_f32_2k"))
-    assert b.query.shape == (1, 8, 64) and b.key_cache.shape == (256, 2, 16, 64)
+    assert b.query.shape == (1, 8, 64) and b.key_cache.shape == (256, 2, 16, 16, 4)
+    assert b.value_cache.shape == (256, 2, 64, 16)
     assert b.block_tables.shape == (1, 128) and b.block_tables.dtype == torch.int32
     assert len(set(b.block_tables[0].tolist())) == 128
     assert b.query.dtype == torch.float32
+
+
+def test_cache_layout_by_definition():
+    """Keys [blocks][Hkv][D / x][16][x] (x = 16 bytes of values), values
+    [blocks][Hkv][D][16]: element (block b, head h, slot t, dim d) checked at its
+    index formula, element by element, against the logical draw."""
+    for dtype, x in (("bf16", 8), ("f32", 4)):
+        spec = wl.custom("layout", 9, dtype, 4, 2, 64, [40, 7], num_blocks=6)
+        b = wl.generate(spec, poison=False)
+        _, kc, vc, _, _ = b.numpy()
+        _, kl, vl, _, _ = b.numpy_logical()
+        kf, vf = kc.reshape(-1), vc.reshape(-1)
+        nb, H, B, D = kl.shape
+        for bb in range(nb):
+            for h in range(H):
+                for t in range(B):
+                    for d in range(D):
+                        ki = (((bb * H + h) * (D // x) + d // x) * B + t) * x + d % x
+                        vi = ((bb * H + h) * D + d) * B + t
+                        assert kf[ki] == kl[bb, h, t, d] and vf[vi] == vl[bb, h, t, d]
+        k2, v2 = wl.pack_kv(kl, vl)
+        assert np.array_equal(k2.view(np.uint8), kc.view(np.uint8))
+        assert np.array_equal(v2.view(np.uint8), vc.view(np.uint8))
