@@ -122,7 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--extras", action="store_true",
-                    help="also time V2 at other partition sizes and V1 (same workload)")
+                    help="also time V2 at other partition sizes, V2 in a single launch and V1 "
+                         "(same workload)")
     ap.add_argument("--no-extras", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
 
@@ -228,7 +229,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "kernel": "attend_kernel<bf16,128,...,false> (V2 Phase 1)",
+                "kernel": "attend_kernel<bf16,128,4,3,kPartials> (V2 Phase 1)",
                 "launch_us_mean": round(p1_us, 2),
                 "launch_us_p10_p90_single": [round(float(np.percentile(durs, 10)), 2),
                                              round(float(np.percentile(durs, 90)), 2)],
@@ -251,6 +252,24 @@ def main():
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / 50
             extras[f"v2_p{other}_us_per_step"] = round(us, 2)
+        ws1 = pa.new_workspace(S, Hq, D, L, P, device=dev)
+
+        def single(i):
+            c = i % len(kcs)
+            pa.pa_decode_v2_single(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws1)
+        try:
+            for i in range(5):
+                single(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(50):
+                single(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            extras[f"v2_single_launch_p{P}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 50, 2)
+        except pa.PagedAttentionError as e:
+            extras[f"v2_single_launch_p{P}_us_per_step"] = f"not applicable: {e}"
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         step(0, "v1")
         e0.record(stream)

@@ -92,16 +92,28 @@ typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *pa_status_string(pa_status_t status);
 
+/* Bytes at the start of every V2 workspace that hold the arrival counters of
+ * pa_decode_v2_single (one uint32 per (sequence, kv head), up to 4096). */
+#define PA_WORKSPACE_HEADER_BYTES 16384
+
 /*
- * Bytes of V2 workspace for this problem: three float32 arrays, each starting
- * on a 256-byte boundary, with P_max = ceil(max_seq_len / partition_size):
- *   tmp_output  [num_seqs][num_q_heads][P_max][head_dim]   at offset 0
+ * Bytes of V2 workspace for this problem: the counter header, then three
+ * float32 arrays, each starting on a 256-byte boundary, with
+ * P_max = ceil(max_seq_len / partition_size):
+ *   header      PA_WORKSPACE_HEADER_BYTES                  at offset 0
+ *   tmp_output  [num_seqs][num_q_heads][P_max][head_dim]   at *tmp_output_offset
  *   exp_sums    [num_seqs][num_q_heads][P_max]             at *exp_sums_offset
  *   max_logits  [num_seqs][num_q_heads][P_max]             at *max_logits_offset
- * max_logits holds the largest scaled logit of each partition (natural-log
- * units); exp_sums holds sum_t exp(z_t - max_logit) over the partition;
- * tmp_output holds the partition's normalised output sum_t exp(z_t - m) v_t / s.
- * (The pre-allocated intermediates of commit 490ff98, "Three changes", item 2.)
+ * After pa_decode_v2_partials, max_logits holds the largest scaled logit of
+ * each partition (natural-log units), exp_sums holds sum_t exp(z_t - max_logit)
+ * over the partition, and tmp_output holds the partition's normalised output
+ * sum_t exp(z_t - m) v_t / s.  (The pre-allocated intermediates of commit
+ * 490ff98, "Three changes", item 2.)
+ * The header must be zero before the workspace's first use by
+ * pa_decode_v2_single (pa_workspace_init, or any zero fill of the buffer);
+ * every call leaves it zero again, whatever the problem shape, so one
+ * workspace serves calls of any shape that fits it.  The other entry points
+ * neither read nor write the header.
  * Returns 0 when there is nothing to hold (num_seqs or max_seq_len is 0) or
  * when the arguments are invalid (negative sizes, partition_size not a
  * positive multiple of 16).
@@ -112,8 +124,14 @@ size_t pa_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_se
 /* Offsets of the workspace arrays described at pa_workspace_size.  Any output
  * pointer may be NULL.  Returns PA_ERR_INVALID_SHAPE for invalid sizes. */
 pa_status_t pa_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
-                                int partition_size, size_t *exp_sums_offset,
-                                size_t *max_logits_offset, int *max_partitions);
+                                int partition_size, size_t *tmp_output_offset,
+                                size_t *exp_sums_offset, size_t *max_logits_offset,
+                                int *max_partitions);
+
+/* Zeroes the counter header of a workspace (workspace_bytes >=
+ * PA_WORKSPACE_HEADER_BYTES, 16-byte aligned), with a small fill kernel on
+ * `stream`.  Needed once per workspace, before its first pa_decode_v2_single. */
+pa_status_t pa_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * V1: single pass.  One workgroup per (sequence, kv head) walks all of the
@@ -129,14 +147,15 @@ pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
                          int max_seq_len, float scale, pa_dtype_t dtype, void *stream);
 
 /*
- * V2: split-KV.  Phase 1, one workgroup per (partition, kv head, sequence),
- * writes each partition's partials into the workspace; Phase 2, one workgroup
- * per (query head, sequence), merges them into out (commit 15ef28e, "[OPT]
- * PagedAttention V2 implementation", Phase 1 and Phase 2).  Two launches on
- * `stream`, no host synchronisation.  workspace_bytes must be at least
- * pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
- * partition_size); the workspace may be reused by later calls on the same
- * stream.  A sequence with L == 0 gets an all-zero output row.
+ * V2: split-KV.  Phase 1, one workgroup per (partition group, kv head,
+ * sequence), writes each partition's partials into the workspace; Phase 2, one
+ * workgroup per (query head, sequence), merges them into out (commit 15ef28e,
+ * "[OPT] PagedAttention V2 implementation", Phase 1 and Phase 2).  Two
+ * launches on `stream`, no host synchronisation.  workspace_bytes must be at
+ * least pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+ * partition_size) and the workspace 16-byte aligned; it may be reused by later
+ * calls on the same stream, but two calls in flight at once must not share it.
+ * A sequence with L == 0 gets an all-zero output row.
  */
 pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          const void *value_cache, const int32_t *block_tables,
@@ -144,6 +163,30 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                          int max_seq_len, float scale, pa_dtype_t dtype, int partition_size,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * V2 in a single launch: the same partitions, each computed as in Phase 1, but
+ * every workgroup folds the partitions it computed into one partial with the
+ * Phase-2 rescale, and the last workgroup of each (sequence, kv head) to
+ * finish -- found with an arrival counter in the workspace header -- merges
+ * those partials in a fixed order and writes out.  Commit 490ff98 (the
+ * StableReductionOrder paragraph) sets a one-kernel atomic merge against a
+ * two-kernel stable one; this is one kernel with a fixed merge order, so its
+ * results are reproducible bit for bit (they differ from pa_decode_v2's only
+ * in rounding order).  Same arguments and workspace as pa_decode_v2, whose
+ * header must be zero before the first call (see pa_workspace_size).  Returns
+ * PA_ERR_UNSUPPORTED, having launched nothing, when num_seqs * num_kv_heads >
+ * 4096 or when (num_q_heads / num_kv_heads) times the number of workgroups per
+ * (sequence, kv head) exceeds 2048.  On MI355X the two launches of
+ * pa_decode_v2 measured faster; this form is for callers that need one launch.
+ */
+pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_seq_len, float scale,
+                                pa_dtype_t dtype, int partition_size, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
  * for partitions p < ceil(L / partition_size) of each sequence; other entries

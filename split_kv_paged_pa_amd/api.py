@@ -7,7 +7,8 @@ call raises.
 
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
-pa_workspace_layout, pa_select_v2, pa_status_string.
+pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_decode_v2_single,
+pa_status_string.
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
 BLOCK_SIZE = 16
 
 PA_OK = 0
+WORKSPACE_HEADER_BYTES = 16384  # PA_WORKSPACE_HEADER_BYTES
 _DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 _lib = None
 
@@ -48,14 +50,18 @@ def load_library():
     lib.pa_workspace_size.argtypes = [I, I, I, I, I]
     lib.pa_workspace_size.restype = Z
     lib.pa_workspace_layout.argtypes = [I, I, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z),
-                                        ctypes.POINTER(I)]
+                                        ctypes.POINTER(Z), ctypes.POINTER(I)]
     lib.pa_workspace_layout.restype = I
+    lib.pa_workspace_init.argtypes = [P, Z, P]
+    lib.pa_workspace_init.restype = I
     lib.pa_select_v2.argtypes = [I, I, I, I]
     lib.pa_select_v2.restype = I
     lib.pa_decode_v1.argtypes = [P] + common + [P]
     lib.pa_decode_v1.restype = I
     lib.pa_decode_v2.argtypes = [P] + common + [I, P, Z, P]
     lib.pa_decode_v2.restype = I
+    lib.pa_decode_v2_single.argtypes = [P] + common + [I, P, Z, P]
+    lib.pa_decode_v2_single.restype = I
     lib.pa_decode.argtypes = [P] + common + [I, P, Z, P]
     lib.pa_decode.restype = I
     lib.pa_decode_v2_partials.argtypes = common + [I, P, Z, P]
@@ -77,14 +83,20 @@ def pa_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_le
 
 
 def pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size):
-    """(exp_sums_offset, max_logits_offset, max_partitions) in bytes / count."""
-    e, m, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int()
+    """(tmp_output_offset, exp_sums_offset, max_logits_offset, max_partitions) in bytes / count."""
+    t, e, m, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int()
     st = load_library().pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len,
-                                            partition_size, ctypes.byref(e), ctypes.byref(m),
-                                            ctypes.byref(n))
+                                            partition_size, ctypes.byref(t), ctypes.byref(e),
+                                            ctypes.byref(m), ctypes.byref(n))
     if st != PA_OK:
         raise PagedAttentionError(st, "pa_workspace_layout")
-    return int(e.value), int(m.value), int(n.value)
+    return int(t.value), int(e.value), int(m.value), int(n.value)
+
+
+def pa_workspace_init(workspace, stream=None):
+    """Zero the counter header of a workspace (needed once, before its first pa_decode_v2)."""
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_workspace_init(wp, wb, _stream(stream)), "pa_workspace_init")
 
 
 def pa_select_v2(max_seq_len: int, num_seqs: int, num_kv_heads: int, partition_size: int) -> bool:
@@ -175,6 +187,20 @@ def pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, sca
            "pa_decode_v2")
 
 
+def pa_decode_v2_single(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
+                        max_seq_len, partition_size, workspace, stream=None):
+    """V2 in one launch (the workspace header must be zero before the first call;
+    new_workspace returns it zeroed).  Raises PagedAttentionError with
+    PA_ERR_UNSUPPORTED when the problem does not fit the single-launch merge."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2_single(o, *args, int(partition_size), wp, wb,
+                                              _stream(stream)), "pa_decode_v2_single")
+
+
 def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
               partition_size, workspace, stream=None):
     """V1 or V2 as pa_select_v2 decides."""
@@ -210,18 +236,20 @@ def pa_decode_v2_reduce(out, seq_lens, max_seq_len, partition_size, workspace, s
 
 
 def new_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, device="cuda"):
-    """A uint8 device tensor of pa_workspace_size bytes (at least 1 byte)."""
+    """A zero-filled uint8 device tensor of pa_workspace_size bytes (at least the
+    counter header), ready for every V2 entry point."""
     n = pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, WORKSPACE_HEADER_BYTES), dtype=torch.uint8, device=device)
 
 
 def workspace_views(workspace, num_seqs, num_q_heads, head_dim, max_seq_len, partition_size):
     """(tmp_out [S,Hq,Pmax,D], exp_sums [S,Hq,Pmax], max_logits [S,Hq,Pmax]) float32 views."""
-    e_off, m_off, n = pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len,
-                                          partition_size)
+    t_off, e_off, m_off, n = pa_workspace_layout(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                                 partition_size)
     rows = num_seqs * num_q_heads * n
     f = workspace.view(torch.uint8)
-    tmp = f[:rows * head_dim * 4].view(torch.float32).view(num_seqs, num_q_heads, n, head_dim)
+    tmp = f[t_off:t_off + rows * head_dim * 4].view(torch.float32).view(num_seqs, num_q_heads, n,
+                                                                        head_dim)
     es = f[e_off:e_off + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, n)
     ml = f[m_off:m_off + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, n)
     return tmp, es, ml

@@ -20,6 +20,10 @@ constexpr int kMaxGridYZ = 65535;
 // ("THE SINGLE HIGHEST-IMPACT CODE CHANGE") and commit 490ff98 ("Three changes").
 constexpr int kV2MinSeqLen = 8192;
 constexpr size_t kAlign = 256;
+// Arrival counters of the single-launch V2, one per (sequence, kv head), at the
+// start of every workspace.
+constexpr size_t kHeaderBytes = PA_WORKSPACE_HEADER_BYTES;
+constexpr long long kTicketSlots = (long long)(kHeaderBytes / sizeof(uint32_t));
 
 // Phase 1 groups consecutive partitions of one (sequence, kv head) into one
 // workgroup when there are few partitions overall (at most kGroupFewUnits per
@@ -56,7 +60,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
     int max_parts;
-    size_t exp_off, max_off, total;
+    size_t tmp_off, exp_off, max_off, total;
 };
 
 // Workspace layout; false if the sizes are invalid.
@@ -72,7 +76,8 @@ bool layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, int pa
     const unsigned long long vec = rows * sizeof(float);
     if (rows && (tmp / rows / sizeof(float) != (unsigned long long)head_dim)) return false;
     out->max_parts = (int)parts;
-    out->exp_off = align_up(tmp);
+    out->tmp_off = kHeaderBytes;
+    out->exp_off = out->tmp_off + align_up(tmp);
     out->max_off = out->exp_off + align_up(vec);
     out->total = rows ? out->max_off + align_up(vec) : 0;
     return true;
@@ -139,7 +144,8 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     if (lay.total > 0 && !workspace) return PA_ERR_NULL_POINTER;
     if (lay.total > 0 && !aligned16(workspace)) return PA_ERR_INVALID_ARGUMENT;
     char *base = static_cast<char *>(workspace);
-    parts->tmp_out = reinterpret_cast<float *>(base);
+    parts->tickets = reinterpret_cast<uint32_t *>(base);
+    parts->tmp_out = reinterpret_cast<float *>(base + lay.tmp_off);
     parts->exp_sums = reinterpret_cast<float *>(base + lay.exp_off);
     parts->max_logits = reinterpret_cast<float *>(base + lay.max_off);
     parts->partition_size = partition_size;
@@ -149,6 +155,15 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
 }
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// The single launch applies when every (sequence, kv head) has a counter slot
+// and the last workgroup's merge fits its weight table.
+bool fused_fits(int num_seqs, int num_q_heads, int num_kv_heads, const pa::Partials &parts) {
+    if (parts.max_parts <= 0) return false;
+    if ((long long)num_seqs * num_kv_heads > kTicketSlots) return false;
+    const long long groups = (parts.max_parts + parts.per_group - 1) / parts.per_group;
+    return (long long)(num_q_heads / num_kv_heads) * groups <= pa::fused_merge_capacity();
+}
 
 }  // namespace
 
@@ -176,15 +191,26 @@ size_t pa_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_se
 }
 
 pa_status_t pa_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
-                                int partition_size, size_t *exp_sums_offset,
-                                size_t *max_logits_offset, int *max_partitions) {
+                                int partition_size, size_t *tmp_output_offset,
+                                size_t *exp_sums_offset, size_t *max_logits_offset,
+                                int *max_partitions) {
     Layout lay;
     if (!layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &lay))
         return PA_ERR_INVALID_SHAPE;
+    if (tmp_output_offset) *tmp_output_offset = lay.tmp_off;
     if (exp_sums_offset) *exp_sums_offset = lay.exp_off;
     if (max_logits_offset) *max_logits_offset = lay.max_off;
     if (max_partitions) *max_partitions = lay.max_parts;
     return PA_OK;
+}
+
+pa_status_t pa_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (workspace_bytes < kHeaderBytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARGUMENT;
+    return from_hip(pa::launch_zero_words(static_cast<uint32_t *>(workspace),
+                                          (int)(kHeaderBytes / sizeof(uint32_t)),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int pa_select_v2(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {
@@ -275,6 +301,33 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
     }
     return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
                                       pb.dtype, parts, out, hs));
+}
+
+pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_seq_len, float scale,
+                                pa_dtype_t dtype, int partition_size, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    pa::Partials parts;
+    st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
+               workspace, workspace_bytes, &parts);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!out) return PA_ERR_NULL_POINTER;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (parts.max_parts == 0)  // no tokens anywhere: the reduce alone writes the zero rows
+        return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
+                                          pb.dtype, parts, out, hs));
+    if (!fused_fits(num_seqs, num_q_heads, num_kv_heads, parts)) return PA_ERR_UNSUPPORTED;
+    return from_hip(pa::launch_fused(pb, parts, out, hs));
 }
 
 pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,

@@ -177,20 +177,118 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ float from_float(float x) { return x; }
 };
 
+constexpr int kMergeCap = 2048;  // group partials (heads x groups) one fused merge can weigh
+
 // ---------------------------------------------------------------------------
-// Phase 1 (kFinal = false): workgroup (pg, kv head, sequence) handles the
-// partitions p in [pg * ppw, min((pg + 1) * ppw, ceil(L / P))) of that sequence
-// and kv head, one after the other, and writes each one's partials.  V1
-// (kFinal = true): workgroup (0, kv head, sequence) covers the whole sequence
-// as a single partition and writes the output.
+// Fused-V2 final merge, run by the last workgroup of a (sequence, kv head):
+// for each of its G query heads, the n group partials {m_i, s_i, o_i} are merged
+// as in Phase 2 -- M = max_i m_i, w_i = exp(m_i - M) s_i, out = sum_i w_i o_i /
+// sum_i w_i -- in increasing i, so the result does not depend on which
+// workgroup ran last.  G * n <= kMergeCap.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int U, bool kFinal>
+template <typename T, int D, int NW>
+__device__ __forceinline__ void merge_groups(const float *__restrict__ tmp_out,
+                                             const float *__restrict__ exp_sums,
+                                             const float *__restrict__ max_logits, size_t head0,
+                                             int group, int n, int max_parts, T *__restrict__ orow) {
+    using M = Mma<T>;
+    constexpr int NTH = NW * 64;
+    constexpr int kPer = kMergeCap / NTH;  // entries per thread
+    __shared__ float sm_w[kMergeCap];
+    __shared__ float sm_hm[16];
+    __shared__ float sm_hw[16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int total = group * n;
+    // Entry e = g * n + i: max logit and exp-sum of group partial i of head g.
+    float es_r[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = tid + k * NTH;
+        es_r[k] = 0.f;
+        if (e < total) {
+            const int gg = e / n;
+            const size_t row = (head0 + gg) * max_parts + (e - gg * n);
+            sm_w[e] = max_logits[row];
+            es_r[k] = exp_sums[row];
+        }
+    }
+    __syncthreads();
+    for (int gg = w; gg < group; gg += NW) {
+        float mx = -INFINITY;
+        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sm_w[gg * n + i]);
+        mx = wave_max(mx);
+        if (lane == 0) sm_hm[gg] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = tid + k * NTH;
+        if (e < total) {
+            const float m = sm_w[e];
+            const float mx = sm_hm[e / n];
+            sm_w[e] = m == -INFINITY ? 0.f : exp_e(m - mx) * es_r[k];
+        }
+    }
+    __syncthreads();
+    for (int gg = w; gg < group; gg += NW) {
+        // Fixed-order sum: lane partials over i = lane, lane + 64, ..., then lanes in order.
+        float sum = 0.f;
+        for (int i = lane; i < n; i += 64) sum += sm_w[gg * n + i];
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        if (lane == 0) sm_hw[gg] = sum;
+    }
+    __syncthreads();
+    // out[g][4c .. 4c+3] = sum_i w_i o_i[4c ..] / W_g, i in increasing order.
+    constexpr int C4 = D / 4;
+    for (int q = tid; q < group * C4; q += NTH) {
+        const int gg = q / C4;
+        const int c = q - gg * C4;
+        const float *src = tmp_out + (head0 + gg) * (size_t)max_parts * D + 4 * c;
+        const float *wt = sm_w + gg * n;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const f32x4 *>(src + (size_t)(i + r) * D);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) a += wt[i + r] * v[r];
+        }
+        for (; i < n; ++i) a += wt[i] * *reinterpret_cast<const f32x4 *>(src + (size_t)i * D);
+        const float W = sm_hw[gg];
+        const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) orow[gg * D + 4 * c + r] = M::from_float(a[r] * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Three schedules of one kernel (MODE):
+//   kPartials (V2 Phase 1): workgroup (pg, kv head, sequence) handles the
+//     partitions p in [pg * ppw, min((pg + 1) * ppw, ceil(L / P))) of that
+//     sequence and kv head, one after the other, and writes each one's partials.
+//   kFused (V2 in one launch): the same partitions, each computed exactly as in
+//     kPartials, but folded into one group partial {max, exp-sum, output} per
+//     head with the Phase-2 rescale; the workgroup writes that, takes a ticket
+//     for its (sequence, kv head), and the last one to arrive merges the group
+//     partials of all workgroups of that (sequence, kv head) in a fixed order
+//     and writes the output.
+//   kSinglePass (V1): workgroup (0, kv head, sequence) covers the whole sequence
+//     as a single partition and writes the output.
+// ---------------------------------------------------------------------------
+enum Mode { kSinglePass = 0, kPartials = 1, kFused = 2 };
+
+template <typename T, int D, int NW, int U, int MODE>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
     int num_kv_heads, int group, int num_blocks, int max_blocks, int max_seq_len, float scale,
     int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
-    float *__restrict__ exp_sums, float *__restrict__ max_logits, T *__restrict__ out) {
+    float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
+    T *__restrict__ out) {
+    constexpr bool kFinal = MODE == kSinglePass;
     using M = Mma<T>;
     constexpr int E = M::E;
     using VU = typename M::VU;
@@ -202,6 +300,13 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __shared__ float sm_l[NW][16];
     __shared__ float sm_f[NW][16];
     __shared__ float sm_o[NW][16][LDS_STRIDE];
+    // kFused: the group partial {max, exp-sum, unnormalised output} per head.
+    constexpr int GA = MODE == kFused ? 16 : 1;
+    __shared__ float sm_gm[GA];
+    __shared__ float sm_gw[GA];
+    __shared__ float sm_gs[GA];  // rescale of sm_ga for the partition being folded in
+    __shared__ float sm_ga[GA][MODE == kFused ? D : 1];
+    __shared__ uint32_t sm_ticket;
 
     const int lane = threadIdx.x & 63;
     // Wave index, made provably uniform so that everything derived from it (the
@@ -226,7 +331,22 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         const int parts = (nblk + bp - 1) / bp;
         p_begin = blockIdx.x * ppw;
         p_end = min(p_begin + ppw, parts);
-        if (p_begin >= p_end) return;  // uniform over the workgroup
+        if (p_begin >= p_end) {  // uniform over the workgroup
+            if (MODE == kFused && parts == 0 && blockIdx.x == 0) {
+                // No workgroup of this (sequence, kv head) has work: L == 0 gives zeros.
+                T *orow = out + ((size_t)s * num_q_heads + (size_t)kvh * group) * D;
+                for (int idx = threadIdx.x; idx < group * D; idx += NW * 64)
+                    orow[idx] = M::from_float(0.f);
+            }
+            return;
+        }
+    }
+    if (MODE == kFused) {
+        for (int idx = threadIdx.x; idx < 16 * D; idx += NW * 64) sm_ga[idx / D][idx % D] = 0.f;
+        if (threadIdx.x < 16) {
+            sm_gm[threadIdx.x] = -INFINITY;
+            sm_gw[threadIdx.x] = 0.f;
+        }
     }
     auto part_end = [&](int p) { return min((p + 1) * bp, nblk); };  // end block of partition p
 
@@ -383,13 +503,27 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[ww][gg] - mx);
                 total += f[ww] * sm_l[ww][gg];
             }
-            const float inv = total > 0.f ? 1.f / total : 0.f;
+            if (MODE == kFused) {
+                // Fold (mx, total, sum_w f_w o_w) into the group partial with the
+                // Phase-2 rescale: weights exp(m - M') against the new group max M'.
+                const float gm = sm_gm[gg];
+                const float gm_new = fmaxf(gm, mx);
+                const float a = gm == -INFINITY ? 0.f : exp_e(gm - gm_new);
+                const float b = mx == -INFINITY ? 0.f : exp_e(mx - gm_new);
+                sm_gm[gg] = gm_new;
+                sm_gw[gg] = sm_gw[gg] * a + total * b;
+                sm_gs[gg] = a;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
-            if (!kFinal && gg < group) {
-                const size_t row = (head0 + gg) * max_parts + p;
-                exp_sums[row] = total;
-                max_logits[row] = mx;
+                for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * b;
+            } else {
+                const float inv = total > 0.f ? 1.f / total : 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
+                if (!kFinal && gg < group) {
+                    const size_t row = (head0 + gg) * max_parts + p;
+                    exp_sums[row] = total;
+                    max_logits[row] = mx;
+                }
             }
         }
         __syncthreads();
@@ -399,7 +533,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             float o = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) o += sm_f[ww][gg] * sm_o[ww][gg][d];
-            if (kFinal) {
+            if (MODE == kFused) {
+                sm_ga[gg][d] = sm_ga[gg][d] * sm_gs[gg] + o;  // same thread owns (gg, d) every time
+            } else if (kFinal) {
                 out[(head0 + gg) * D + d] = M::from_float(o);
             } else {
                 tmp_out[((head0 + gg) * max_parts + p) * D + d] = o;
@@ -440,6 +576,47 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         if (done) break;
     }
     while (a_p < p_end) finish(a_p++);
+    if (MODE != kFused) return;
+
+    // ---- kFused epilogue.  Group partial g of this workgroup goes to entry gi =
+    // blockIdx.x of the workspace partials (normalised like a partition partial).
+    const size_t head0 = (size_t)s * num_q_heads + (size_t)kvh * group;
+    const int gi = blockIdx.x;
+    __syncthreads();
+    // Publication: the group partial is stored with device-scope atomic stores
+    // (written through to the device's point of coherence), each wave waits until
+    // its stores have completed, and only then is the ticket taken.  No cache
+    // writeback is needed: nothing else this workgroup wrote is read elsewhere.
+    if (threadIdx.x < group) {
+        const size_t row = (head0 + threadIdx.x) * max_parts + gi;
+        __hip_atomic_store(exp_sums + row, sm_gw[threadIdx.x], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(max_logits + row, sm_gm[threadIdx.x], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int idx = threadIdx.x; idx < group * D; idx += NW * 64) {
+        const int gg = idx / D;
+        const int d = idx - gg * D;
+        const float W = sm_gw[gg];
+        __hip_atomic_store(tmp_out + ((head0 + gg) * max_parts + gi) * D + d,
+                           W > 0.f ? sm_ga[gg][d] / W : 0.f, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();
+    uint32_t *ticket = tickets + (size_t)s * num_kv_heads + kvh;
+    if (threadIdx.x == 0)
+        sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int parts = (nblk + bp - 1) / bp;
+    const int n = (parts + ppw - 1) / ppw;  // workgroups of this (sequence, kv head) with work
+    if ((int)sm_ticket != n - 1) return;    // uniform: not the last to arrive
+    // Acquire: drop this device's cached copies of lines other workgroups wrote.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_groups<T, D, NW>(tmp_out, exp_sums, max_logits, head0, group, n, max_parts,
+                           out + head0 * D);
+    if (threadIdx.x == 0)  // leave the counter zero for the next call
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,35 +723,42 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     }
 }
 
+__global__ void zero_words_kernel(uint32_t *__restrict__ p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 constexpr int kWaves = 4;
 constexpr int kReduceWaves = 16;
 
 // Blocks in flight per wave: three when a block's K and V fit in 32 VGPRs.
 template <typename T, int D> constexpr int prefetch_depth() { return D * sizeof(T) <= 256 ? 3 : 2; }
 
-template <typename T, int D, bool kFinal>
+template <typename T, int D, int MODE>
 hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
+    constexpr bool kFinal = MODE == kSinglePass;
     const int group = pb.num_q_heads / pb.num_kv_heads;
     const int ppw = kFinal ? 1 : parts->per_group;
     dim3 grid(kFinal ? 1 : (parts->max_parts + ppw - 1) / ppw, pb.num_kv_heads, pb.num_seqs);
-    attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), kFinal><<<grid, kWaves * 64, 0, stream>>>(
+    attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), MODE><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
         pb.num_kv_heads, group, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
         kFinal ? kBlockTokens : parts->partition_size, ppw, kFinal ? 0 : parts->max_parts,
         kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
-        kFinal ? nullptr : parts->max_logits, static_cast<T *>(out));
+        kFinal ? nullptr : parts->max_logits, MODE == kFused ? parts->tickets : nullptr,
+        static_cast<T *>(out));
     return hipGetLastError();
 }
 
-template <bool kFinal>
+template <int MODE>
 hipError_t dispatch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
     if (pb.dtype == Dtype::BF16) {
-        return pb.head_dim == 64 ? launch_attend<uint16_t, 64, kFinal>(pb, parts, out, stream)
-                                 : launch_attend<uint16_t, 128, kFinal>(pb, parts, out, stream);
+        return pb.head_dim == 64 ? launch_attend<uint16_t, 64, MODE>(pb, parts, out, stream)
+                                 : launch_attend<uint16_t, 128, MODE>(pb, parts, out, stream);
     }
-    return pb.head_dim == 64 ? launch_attend<float, 64, kFinal>(pb, parts, out, stream)
-                             : launch_attend<float, 128, kFinal>(pb, parts, out, stream);
+    return pb.head_dim == 64 ? launch_attend<float, 64, MODE>(pb, parts, out, stream)
+                             : launch_attend<float, 128, MODE>(pb, parts, out, stream);
 }
 
 template <typename T, int D>
@@ -591,11 +775,22 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
 }  // namespace
 
 hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream) {
-    return dispatch_attend<true>(pb, nullptr, out, stream);
+    return dispatch_attend<kSinglePass>(pb, nullptr, out, stream);
 }
 
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream) {
-    return dispatch_attend<false>(pb, &parts, nullptr, stream);
+    return dispatch_attend<kPartials>(pb, &parts, nullptr, stream);
+}
+
+hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hipStream_t stream) {
+    return dispatch_attend<kFused>(pb, &parts, out, stream);
+}
+
+int fused_merge_capacity() { return kMergeCap; }
+
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t stream) {
+    zero_words_kernel<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,

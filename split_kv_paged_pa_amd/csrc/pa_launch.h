@@ -28,6 +28,7 @@ struct Partials {
     float *tmp_out;      // [S][Hq][max_parts][D]
     float *exp_sums;     // [S][Hq][max_parts]
     float *max_logits;   // [S][Hq][max_parts]
+    uint32_t *tickets;   // [S][Hkv] arrival counters of the fused form (zero between calls)
     int partition_size;
     int max_parts;
     int per_group;   // consecutive partitions handled by one Phase-1 workgroup
@@ -37,6 +38,13 @@ struct Partials {
 hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream);
 // V2 Phase 1: one workgroup per (partition, kv head, sequence) -> partials.
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream);
+// V2 in one launch: the Phase-1 grid; each workgroup folds its partitions into a
+// group partial, and the last workgroup of each (sequence, kv head) merges them -> out.
+// Needs group * ceil(max_parts / per_group) <= fused_merge_capacity().
+hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hipStream_t stream);
+int fused_merge_capacity();
+// n uint32 zeros at p (a plain fill kernel).
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t stream);
 // V2 Phase 2: one workgroup per (query head, sequence): partials -> out.
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
                          int max_seq_len, Dtype dtype, const Partials &parts, void *out,

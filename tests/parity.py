@@ -46,6 +46,7 @@ class DeviceBatch:
                               self.max_seq_len, P)
         if poison:
             ws.view(torch.uint8).fill_(0xFF)  # all-ones float32 words are NaN
+            pa.pa_workspace_init(ws)          # the counter header must start at zero
         return ws
 
     def run_v2(self, P, ws=None):

@@ -38,15 +38,18 @@ def test_status_strings():
 
 def test_workspace_size_arithmetic():
     # 100000 tokens, 32 query heads, D 128: 196 partitions of 512, 98 of 1024.
+    # Layout: the 16 KiB counter header, then tmp_output, exp_sums, max_logits,
+    # each rounded up to 256 bytes.
     def expect(S, Hq, D, L, P):
         n = -(-L // P)
         a = lambda x: -(-x // 256) * 256
         rows = S * Hq * n
-        return a(rows * D * 4) + 2 * a(rows * 4) if rows else 0
-    assert pa.pa_workspace_size(1, 32, 128, 100000, 512) == expect(1, 32, 128, 100000, 512) == 3261440
-    assert pa.pa_workspace_size(1, 32, 128, 100000, 1024) == 1630720
-    assert pa.pa_workspace_layout(1, 32, 128, 100000, 1024)[2] == 98
-    assert pa.pa_workspace_layout(1, 32, 128, 100000, 512)[2] == 196
+        return 16384 + a(rows * D * 4) + 2 * a(rows * 4) if rows else 0
+    assert pa.pa_workspace_size(1, 32, 128, 100000, 512) == expect(1, 32, 128, 100000, 512) == 3277824
+    assert pa.pa_workspace_size(1, 32, 128, 100000, 1024) == 1647104
+    assert pa.pa_workspace_layout(1, 32, 128, 100000, 1024) == (16384, 16384 + 1605632,
+                                                               16384 + 1605632 + 12544, 98)
+    assert pa.pa_workspace_layout(1, 32, 128, 100000, 512)[3] == 196
     assert pa.pa_workspace_size(16, 32, 128, 32768, 1024) == expect(16, 32, 128, 32768, 1024)
     assert pa.pa_workspace_size(0, 32, 128, 1000, 512) == 0
     assert pa.pa_workspace_size(3, 32, 128, 0, 512) == 0
@@ -139,3 +142,15 @@ def test_binding_checks_the_split_layout():
     with pytest.raises(ValueError, match="expected"):
         pa.pa_decode_v1(torch.zeros_like(q), q, vc, vc, torch.zeros(1, 4, dtype=torch.int32),
                         torch.ones(1, dtype=torch.int32), 0.125, 1)
+
+
+def test_workspace_init_and_launch_count_checks():
+    lib = pa.load_library()
+    lib.pa_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.pa_workspace_init(None, 1 << 20, None) == NULLP
+    assert lib.pa_workspace_init(FAKE, 16383, None) == WS
+    assert lib.pa_workspace_init(FAKE + 4, 1 << 20, None) == ARG
+    # pa_decode_v2_single refuses, before launching, problems the merge cannot take:
+    # 625 * 8 = 5000 (sequence, kv head) pairs, more than the 4096 header counters.
+    big = (FAKE, FAKE, FAKE, FAKE, FAKE, 625, 64, 8, 128, 16, 100, 2048, 20000, 0.088, 1)
+    assert lib.pa_decode_v2_single(FAKE, *big, 1024, FAKE, 1 << 40, None) == UNSUP

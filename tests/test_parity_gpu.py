@@ -236,6 +236,89 @@ def test_dispatch_threshold():
 
 
 # ---------------------------------------------------------------------------
+# Single-launch V2 (pa_decode_v2_single): the last workgroup of each
+# (sequence, kv head) merges.
+# ---------------------------------------------------------------------------
+FUSED = [  # name, dtype, Hq, Hkv, D, lens, P
+    ("ragged_bf16", "bf16", 32, 4, 128, EDGE_LENS, 512),
+    ("gqa5", "bf16", 40, 8, 128, [3000, 1, 700, 0, 4097], 256),
+    ("f32_d64", "f32", 8, 2, 64, [5000, 16, 17], 128),
+    ("grouped_long", "bf16", 64, 8, 128, [20000], 512),
+    ("g16_d128", "bf16", 16, 1, 128, [9000, 33], 64),
+    ("long_100k_shape", "bf16", 32, 4, 128, [100000], 1024),
+]
+
+
+def _header(ws):
+    return ws.view(torch.uint8)[:pa.api.WORKSPACE_HEADER_BYTES].cpu()
+
+
+def run_single(db, P, ws):
+    out = db.new_out()
+    pa.pa_decode_v2_single(out, *db.args(), P, ws)
+    return out
+
+
+@pytest.mark.parametrize("name,dtype,Hq,Hkv,D,lens,P", FUSED, ids=[f[0] for f in FUSED])
+def test_single_launch_v2(name, dtype, Hq, Hkv, D, lens, P):
+    """One launch against the oracle and against pa_decode_v2 on the same inputs;
+    bitwise repeatable; the counter header is zero again afterwards."""
+    spec = wl.custom(name, 113, dtype, Hq, Hkv, D, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    print(f"[case] single launch {name}", flush=True)
+    ref = oracle_out(b)
+    ws = db.workspace(P)
+    out = run_single(db, P, ws)
+    assert_close(to_f64(out), ref, dtype, f"single launch {name}")
+    assert torch.count_nonzero(_header(ws)) == 0, "arrival counters not left at zero"
+    again = run_single(db, P, ws)
+    assert torch.equal(out.view(torch.uint8), again.view(torch.uint8)), "not repeatable"
+    assert_close(to_f64(db.run_v2(P)), ref, dtype, f"two launches {name}")
+
+
+def test_single_launch_workspace_reuse_across_shapes():
+    """One workspace serves calls of different shapes in turn: the counters each call
+    uses are left at zero, so the next shape starts clean."""
+    specs = [wl.custom("reuseA", 114, "bf16", 32, 4, 128, [3000, 900, 17]),
+             wl.custom("reuseB", 115, "bf16", 64, 8, 128, [5000]),
+             wl.custom("reuseC", 116, "f32", 8, 1, 64, [1, 2000, 70, 0, 4000])]
+    P = 256
+    size = max(pa.pa_workspace_size(sp.num_seqs, sp.num_q_heads, sp.head_dim, sp.max_seq_len, P)
+               for sp in specs)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    batches = [wl.generate(sp) for sp in specs]
+    refs = [oracle_out(b) for b in batches]
+    for rnd in range(2):
+        for sp, b, ref in zip(specs, batches, refs):
+            db = DeviceBatch(b)
+            out = run_single(db, P, ws)
+            assert_close(to_f64(out), ref, sp.dtype, f"{sp.name} round {rnd}")
+            assert torch.count_nonzero(_header(ws)) == 0
+
+
+def test_single_launch_refuses_what_does_not_fit():
+    """More group partials than the merge table holds: PA_ERR_UNSUPPORTED, nothing
+    written; pa_decode_v2 handles the same problem."""
+    spec = wl.custom("nofit", 117, "bf16", 16, 2, 128, [12000, 40])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    out = db.new_out()
+    with pytest.raises(pa.PagedAttentionError) as e:
+        pa.pa_decode_v2_single(out, *db.args(), 16, db.workspace(16))
+    assert e.value.status == 3  # PA_ERR_UNSUPPORTED
+    assert torch.isnan(out).all()
+    assert_close(to_f64(db.run_v2(16)), oracle_out(b), "bf16", "two launches, P=16")
+
+
+def test_single_launch_empty_batch_zero_rows():
+    spec = wl.custom("single_empty", 118, "bf16", 8, 2, 128, [0, 0], num_blocks=1)
+    db = DeviceBatch(wl.generate(spec))
+    db.max_seq_len = 0
+    assert np.all(to_f64(run_single(db, 512, db.workspace(512))) == 0)
+
+
+# ---------------------------------------------------------------------------
 # The five named workloads at full size.
 # ---------------------------------------------------------------------------
 FULL = [("tiny_f32_2k", None), ("long_100k_gqa8", None), ("batch16_1k_32k", None),
