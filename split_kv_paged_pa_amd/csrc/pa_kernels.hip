@@ -318,6 +318,12 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const int kvh = blockIdx.y;
     const int s = blockIdx.z;
 
+    // The first block this wave will read does not depend on the sequence length:
+    // its table entry is requested together with seq_lens[s] (index clamped into
+    // the row), so the two scalar loads share one memory latency.
+    const int32_t *bt = block_tables + (size_t)s * max_blocks;
+    const int j_first = (kFinal ? 0 : blockIdx.x * ppw * (partition_size / kBlockTokens)) + w;
+    const int id_first = max_blocks > 0 ? bt[min(j_first, max_blocks - 1)] : 0;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
     // Partitions of this workgroup, in blocks of bp each.
@@ -369,7 +375,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int32_t *bt = block_tables + (size_t)s * max_blocks;
     const size_t slab = (size_t)kBlockTokens * D;        // elements of one (block, kv head) slab
     // Byte offsets inside a (block, kv head) slab.  Keys, [D/E][16][E]: chunk c of
     // lane l is the 16 bytes at 1024*c + 16*l, so each load instruction reads 1 KiB
@@ -397,7 +402,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         }
     };
     settle();
-    int id_next = i_p < p_end ? bt[i_j] : 0;
+    int id_next = i_p < p_end ? (i_j == j_first ? id_first : bt[i_j]) : 0;
 
     // Every issue emits the same loads in the same order -- past the end, or for
     // a block id outside [0, num_blocks), they read the (cached) query row and the
