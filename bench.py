@@ -109,6 +109,63 @@ def hbm_probe(dev):
     return {"unit": "GB/s", **res}
 
 
+DISPATCH_GRID = [(1, 1), (1, 8), (4, 8), (16, 8), (64, 8), (256, 8)]
+DISPATCH_LENS = [512, 1024, 2048, 4096, 8192, 16384]
+
+
+def dispatch_sweep(dev):
+    """V1 against V2 (P = 512, 1024) and the two dispatch rules, over uniform-length
+    bf16 batches (Hq = 8 Hkv, D = 128, random block tables, random values).  Prints
+    one JSON object with a row per (S, Hkv, L): the measured us per call of each
+    form, and the us of the form pa_select_v2 (the pages' rule) and
+    pa_select_v2_auto (the MI355X rule) pick."""
+    G, D = 8, 128
+    st = torch.cuda.current_stream()
+    rows = []
+    for S, Hkv in DISPATCH_GRID:
+        for L in DISPATCH_LENS:
+            nblk = -(-L // 16)
+            NB = S * nblk
+            Hq = Hkv * G
+            gen = torch.Generator(device=dev).manual_seed(S * 100003 + L)
+            q = torch.randn(S, Hq, D, device=dev, generator=gen).to(torch.bfloat16)
+            kc = torch.randn(NB, Hkv, D // 8, 16, 8, device=dev, generator=gen).to(torch.bfloat16)
+            vc = torch.randn(NB, Hkv, D, 16, device=dev, generator=gen).to(torch.bfloat16)
+            bt = torch.randperm(NB, device=dev, generator=gen).to(torch.int32).view(S, nblk)
+            sl = torch.full((S,), L, dtype=torch.int32, device=dev)
+            out = torch.empty_like(q)
+            row = {"S": S, "Hkv": Hkv, "L": L}
+            for name, P in (("v1", None), ("v2_p512", 512), ("v2_p1024", 1024)):
+                ws = None if P is None else pa.new_workspace(S, Hq, D, L, P, device=dev)
+
+                def run():
+                    if P is None:
+                        pa.pa_decode_v1(out, q, kc, vc, bt, sl, 0.088, L)
+                    else:
+                        pa.pa_decode_v2(out, q, kc, vc, bt, sl, 0.088, L, P, ws)
+                for _ in range(3):
+                    run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for _ in range(20):
+                    run()
+                e1.record(st)
+                torch.cuda.synchronize()
+                row[name] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
+            row["pages_rule_us"] = row["v2_p1024"] if pa.pa_select_v2(L, S, Hkv, 1024) else row["v1"]
+            row["auto_rule_us"] = row["v2_p1024"] if pa.pa_select_v2_auto(L, S, Hkv, 1024) else row["v1"]
+            print(f"[sweep] {row}", file=sys.stderr, flush=True)
+            rows.append(row)
+            del q, kc, vc, bt, sl, out
+            torch.cuda.empty_cache()
+    print(json.dumps({"dispatch_sweep": rows, "device": torch.cuda.get_device_name(0),
+                      "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+                      "note": "us per call from HIP events over 20 back-to-back calls; calls under "
+                              "~15 us are bound by the Python launch path, not the GPU"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +182,9 @@ def main():
                     help="also time V2 at other partition sizes, V2 in a single launch and V1 "
                          "(same workload)")
     ap.add_argument("--no-extras", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="instead of the step benchmark, time V1 / V2 over a grid of batch shapes "
+                         "and compare the two dispatch rules")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -137,6 +197,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.dispatch_sweep:
+        dispatch_sweep(dev)
+        return
     spec = wl.config(args.workload)
     P = args.partition_size
     batch = wl.generate(spec)

@@ -225,6 +225,28 @@ pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const
                       pa_dtype_t dtype, int partition_size, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/*
+ * Dispatch rule derived from measurements on MI355X (256 compute units), for the
+ * same choice.  Returns 1 (V2) when max_seq_len > 8192, as pa_select_v2 does:
+ * above that, V1 would leave one long sequence as a straggler, and the host
+ * does not know the individual lengths.  Returns 0 (V1) when
+ * max_seq_len <= 1024.  In between, returns 1 iff the V1 grid, one workgroup per
+ * (sequence, kv head), would occupy fewer than half of the current device's
+ * compute units (2 * num_seqs * num_kv_heads < CUs); there the pages' rule picks
+ * V1, which measured up to 4x slower.  Falls back to pa_select_v2 when the
+ * compute-unit count is unknown.  partition_size is not used.
+ */
+int pa_select_v2_auto(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size);
+
+/* pa_decode_v1 or pa_decode_v2, chosen by pa_select_v2_auto. */
+pa_status_t pa_decode_auto(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                           int partition_size, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,8 +7,8 @@ call raises.
 
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
-pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_decode_v2_single,
-pa_status_string.
+pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_select_v2_auto,
+pa_decode_auto, pa_decode_v2_single, pa_status_string.
 """
 from __future__ import annotations
 
@@ -56,6 +56,10 @@ def load_library():
     lib.pa_workspace_init.restype = I
     lib.pa_select_v2.argtypes = [I, I, I, I]
     lib.pa_select_v2.restype = I
+    lib.pa_select_v2_auto.argtypes = [I, I, I, I]
+    lib.pa_select_v2_auto.restype = I
+    lib.pa_decode_auto.argtypes = [P] + common + [I, P, Z, P]
+    lib.pa_decode_auto.restype = I
     lib.pa_decode_v1.argtypes = [P] + common + [P]
     lib.pa_decode_v1.restype = I
     lib.pa_decode_v2.argtypes = [P] + common + [I, P, Z, P]
@@ -101,6 +105,12 @@ def pa_workspace_init(workspace, stream=None):
 
 def pa_select_v2(max_seq_len: int, num_seqs: int, num_kv_heads: int, partition_size: int) -> bool:
     return bool(load_library().pa_select_v2(max_seq_len, num_seqs, num_kv_heads, partition_size))
+
+
+def pa_select_v2_auto(max_seq_len: int, num_seqs: int, num_kv_heads: int,
+                      partition_size: int) -> bool:
+    return bool(load_library().pa_select_v2_auto(max_seq_len, num_seqs, num_kv_heads,
+                                                 partition_size))
 
 
 def _stream(stream):
@@ -211,6 +221,18 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode(o, *args, int(partition_size), wp, wb, _stream(stream)),
            "pa_decode")
+
+
+def pa_decode_auto(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                   partition_size, workspace, stream=None):
+    """V1 or V2 as pa_select_v2_auto decides (the MI355X-measured rule)."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_auto(o, *args, int(partition_size), wp, wb, _stream(stream)),
+           "pa_decode_auto")
 
 
 def pa_decode_v2_partials(query, key_cache, value_cache, block_tables, seq_lens, scale,

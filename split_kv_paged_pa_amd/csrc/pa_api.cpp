@@ -19,6 +19,9 @@ constexpr int kMaxGridYZ = 65535;
 // V2 is used above this many tokens: the threshold of commit 900ae0b
 // ("THE SINGLE HIGHEST-IMPACT CODE CHANGE") and commit 490ff98 ("Three changes").
 constexpr int kV2MinSeqLen = 8192;
+// Measured on MI355X: V1 (one workgroup per (sequence, kv head)) already wins at
+// or below this many tokens, whatever the batch.
+constexpr int kV1ShortSeqLen = 1024;
 constexpr size_t kAlign = 256;
 // Arrival counters of the single-launch V2, one per (sequence, kv head), at the
 // start of every workspace.
@@ -328,6 +331,33 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                                           pb.dtype, parts, out, hs));
     if (!fused_fits(num_seqs, num_q_heads, num_kv_heads, parts)) return PA_ERR_UNSUPPORTED;
     return from_hip(pa::launch_fused(pb, parts, out, hs));
+}
+
+int pa_select_v2_auto(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {
+    (void)partition_size;
+    if (max_seq_len > kV2MinSeqLen) return 1;
+    if (max_seq_len <= kV1ShortSeqLen) return 0;
+    const int cus = compute_units();
+    if (cus <= 0) return 0;  // unknown device: the pages' rule
+    return 2LL * num_seqs * num_kv_heads < cus ? 1 : 0;
+}
+
+pa_status_t pa_decode_auto(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                           int partition_size, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (pa_select_v2_auto(max_seq_len, num_seqs, num_kv_heads, partition_size)) {
+        return pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                            num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                            max_blocks_per_seq, max_seq_len, scale, dtype, partition_size,
+                            workspace, workspace_bytes, stream);
+    }
+    return pa_decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_seq_len, scale, dtype, stream);
 }
 
 pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,

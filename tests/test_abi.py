@@ -154,3 +154,14 @@ def test_workspace_init_and_launch_count_checks():
     # 625 * 8 = 5000 (sequence, kv head) pairs, more than the 4096 header counters.
     big = (FAKE, FAKE, FAKE, FAKE, FAKE, 625, 64, 8, 128, 16, 100, 2048, 20000, 0.088, 1)
     assert lib.pa_decode_v2_single(FAKE, *big, 1024, FAKE, 1 << 40, None) == UNSUP
+
+
+def test_select_v2_auto_rule():
+    # Above 8192 tokens: V2, as the pages' rule; at or below 1024: V1, whatever the batch.
+    assert pa.pa_select_v2_auto(8193, 256, 8, 1024) is True
+    assert pa.pa_select_v2_auto(1024, 1, 1, 1024) is False
+    # In between the answer depends on the device's compute units (V2 when the V1 grid
+    # would fill less than half of them); without a GPU it falls back to the pages' rule.
+    import torch
+    if not torch.cuda.is_available():
+        assert pa.pa_select_v2_auto(4096, 1, 8, 1024) is False

@@ -318,6 +318,27 @@ def test_single_launch_empty_batch_zero_rows():
     assert np.all(to_f64(run_single(db, 512, db.workspace(512))) == 0)
 
 
+AUTO = [  # lens, Hkv, expected choice on a 256-CU device
+    ([4096, 3000], 8, True),           # 16 units < 128: V2 below the pages' threshold
+    ([2048] * 20, 8, False),           # 160 units >= 128: V1
+    ([700, 1024, 5], 4, False),        # max_seq_len <= 1024: V1
+    ([9000, 12], 2, True),             # above 8192: V2
+]
+
+
+@pytest.mark.parametrize("lens,hkv,v2", AUTO, ids=["few_units", "many_units", "short", "long"])
+def test_decode_auto(lens, hkv, v2):
+    """pa_decode_auto follows the measured MI355X rule and matches the oracle."""
+    spec = wl.custom("auto", 120, "bf16", hkv * 8, hkv, 128, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert pa.pa_select_v2_auto(db.max_seq_len, spec.num_seqs, hkv, 512) is v2
+    out = db.new_out()
+    pa.pa_decode_auto(out, *db.args(), 512, db.workspace(512))
+    assert_close(to_f64(out), oracle_out(b), "bf16", "pa_decode_auto")
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads at full size.
 # ---------------------------------------------------------------------------
