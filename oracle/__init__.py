@@ -8,6 +8,7 @@ pa_oracle.c, computed in float64; this module only marshals numpy arrays.
 Functions
   decode    full-softmax attention (the plain definition; V1 and V2 are both
             schedules of it)
+  decode_q  the same for q_len query tokens per sequence, causal over the cache
   partials  the pages' Phase 1 per-partition statistics (m_p, s_p, o_p)
   merge     the pages' Phase 2 log-sum-exp merge of those partials
 
@@ -46,6 +47,8 @@ def load(path=None):
     lib.pa_oracle_partials.restype = I
     lib.pa_oracle_merge.argtypes = [P, P, P, P, P, I, I, I, I, I]
     lib.pa_oracle_merge.restype = I
+    lib.pa_oracle_decode_q.argtypes = [P, P, P, P, I, P, P, I, I, I, I, I, I, I, ctypes.c_float, I]
+    lib.pa_oracle_decode_q.restype = I
     return lib
 
 
@@ -113,6 +116,27 @@ def decode(query, key_cache, value_cache, block_tables, seq_lens, scale, dtype="
                               float(scale), rp, nr, int(threads))
     if rc:
         raise RuntimeError(f"pa_oracle_decode failed with code {rc}")
+    return out
+
+
+def decode_q(query, key_cache, value_cache, block_tables, seq_lens, scale, dtype="f32",
+             threads=0, lib=None):
+    """fp64 output [S, q_len, Hq, D] of q_len query tokens per sequence ([S, q_len, Hq, D]
+    query): token j attends to cache tokens 0 .. L - q_len + j (zero row if none)."""
+    lib = _load(lib)
+    if not isinstance(query, np.ndarray) or query.ndim != 4:
+        raise ValueError("query must be a [S, q_len, Hq, D] numpy array")
+    S, q_len, Hq, D = query.shape
+    code, _, _, Hkv, _, B, mb = _problem(query.reshape(S, q_len * Hq, D), key_cache, value_cache,
+                                         block_tables, seq_lens, dtype)
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    out = np.empty((S, q_len, Hq, D), np.float64)
+    rc = lib.pa_oracle_decode_q(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), code,
+                                _ptr(block_tables), _ptr(seq_lens), S, q_len, Hq, Hkv, D, B, mb,
+                                float(scale), int(threads))
+    if rc:
+        raise RuntimeError(f"pa_oracle_decode_q failed with code {rc}")
     return out
 
 

@@ -87,6 +87,7 @@ typedef struct {
     const int32_t *block_tables, *seq_lens;
     int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
     double scale;
+    int q_len; /* query tokens per sequence (1 for plain decode) */
 } problem_t;
 
 /* Values per 16-byte group of the key layout. */
@@ -129,10 +130,13 @@ static size_t value_index(const problem_t *pb, int s, int kvh, int t, int d) {
     return (slab * (size_t)pb->head_dim + (size_t)d) * pb->block_size + slot;
 }
 
-/* Scaled logit z_t of query head h of sequence s against token t. */
+/* Scaled logit z_t of query head h of sequence s against token t.  With q_len
+ * query tokens per sequence, h is the combined index j * num_q_heads + head of
+ * query token j ([num_seqs][q_len][num_q_heads] rows). */
 static double logit(const problem_t *pb, int s, int h, int t) {
     int G = pb->num_q_heads / pb->num_kv_heads;
-    size_t qoff = ((size_t)s * pb->num_q_heads + h) * pb->head_dim;
+    size_t qoff = ((size_t)s * pb->q_len * pb->num_q_heads + h) * pb->head_dim;
+    h %= pb->num_q_heads;
     double dot = 0.0;
     for (int d = 0; d < pb->head_dim; ++d)
         dot += elem(pb->query, qoff + d, pb->dtype) *
@@ -147,6 +151,7 @@ static int attend_range(const problem_t *pb, int s, int h, int t0, int t1, doubl
                         double *den) {
     int n = t1 - t0;
     int G = pb->num_q_heads / pb->num_kv_heads;
+    int hv = h % pb->num_q_heads; /* query head of the combined (token, head) index h */
     double *z = (double *)malloc(sizeof(double) * (size_t)n);
     if (!z) return -10;
     double zmax = -INFINITY;
@@ -160,7 +165,7 @@ static int attend_range(const problem_t *pb, int s, int h, int t0, int t1, doubl
         double w = exp(z[t - t0] - zmax);
         sum += w;
         for (int d = 0; d < pb->head_dim; ++d)
-            o[d] += w * elem(pb->value_cache, value_index(pb, s, h / G, t, d), pb->dtype);
+            o[d] += w * elem(pb->value_cache, value_index(pb, s, hv / G, t, d), pb->dtype);
     }
     for (int d = 0; d < pb->head_dim; ++d) o[d] /= sum;
     free(z);
@@ -182,7 +187,7 @@ int pa_oracle_decode(double *out, const void *query, const void *key_cache, cons
                      int num_threads) {
     problem_t pb = {query, key_cache, value_cache, dtype, block_tables, seq_lens,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                    max_blocks_per_seq, (double)scale};
+                    max_blocks_per_seq, (double)scale, 1};
     int rc = check_problem(&pb);
     if (rc) return rc;
     if (!out) return -1;
@@ -235,7 +240,7 @@ int pa_oracle_partials(double *tmp_out, double *exp_sums, double *max_logits, co
                        int num_threads) {
     problem_t pb = {query, key_cache, value_cache, dtype, block_tables, seq_lens,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                    max_blocks_per_seq, (double)scale};
+                    max_blocks_per_seq, (double)scale, 1};
     int rc = check_problem(&pb);
     if (rc) return rc;
     if (!tmp_out || !exp_sums || !max_logits) return -1;
@@ -314,4 +319,54 @@ int pa_oracle_merge(double *out, const double *tmp_out, const double *exp_sums,
         }
     }
     return 0;
+}
+
+/*
+ * Decode of q_len query tokens per sequence (q_len >= 1).  The tokens are the
+ * last q_len positions of the sequence, already in the cache: query token j of
+ * sequence s sits at position L - q_len + j (L = seq_lens[s]) and attends to
+ * the tokens 0 .. L - q_len + j (causal over the cache; the pages batch a
+ * q_len dimension next to the GQA group, commit 490ff98, the summary_statistics
+ * message).  A query token that sees no token (L - q_len + j < 0) gets a zero
+ * row.  query and out are [num_seqs][q_len][num_q_heads][head_dim]; the rest
+ * as pa_oracle_decode.
+ */
+int pa_oracle_decode_q(double *out, const void *query, const void *key_cache,
+                       const void *value_cache, int dtype, const int32_t *block_tables,
+                       const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                       float scale, int num_threads) {
+    problem_t pb = {query, key_cache, value_cache, dtype, block_tables, seq_lens,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, (double)scale, q_len};
+    int rc = check_problem(&pb);
+    if (rc) return rc;
+    if (!out) return -1;
+    if (q_len < 1) return -3;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+    long rows_per_seq = (long)q_len * num_q_heads;
+    long n = (long)num_seqs * rows_per_seq;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < n; ++i) {
+        int s = (int)(i / rows_per_seq);
+        int hj = (int)(i % rows_per_seq); /* j * num_q_heads + h */
+        int j = hj / num_q_heads;
+        double *o = out + (size_t)i * head_dim;
+        int visible = seq_lens[s] - q_len + j + 1; /* tokens 0 .. L - q_len + j */
+        if (visible <= 0) {
+            for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+            continue;
+        }
+        double m, den;
+        if (attend_range(&pb, s, hj, 0, visible, o, &m, &den)) {
+#pragma omp atomic write
+            failed = 1;
+        }
+    }
+    return failed ? -10 : 0;
 }

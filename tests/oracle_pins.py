@@ -277,6 +277,42 @@ def pin_page_counts(lib=None):
         assert abs(ml[0, 0, n - 1] - z.max()) <= 1e-12, f"last partition of P={P}"
 
 
+def pin_multi_query_causal(lib=None):
+    """q_len query tokens per sequence against torch's dense float64 attention with an
+    explicit mask: token j of a length-L sequence sees cache tokens 0 .. L - q_len + j
+    (mask row j = tril with diagonal offset L - q_len); a token that sees nothing is
+    a zero row."""
+    for dtype, D, Hq, Hkv, q_len, lens in (("f32", 64, 8, 2, 3, [1, 2, 3, 17, 40, 0]),
+                                            ("bf16", 128, 8, 8, 2, [16, 33, 300]),
+                                            ("bf16", 64, 4, 1, 4, [5, 64, 129])):
+        spec = wl.custom("multiq", 22, dtype, Hq, Hkv, D, lens)
+        b = wl.generate(spec)
+        q1, kc, vc, bt, sl = b.numpy()
+        _, kl, vl, _, _ = b.numpy_logical()
+        S = spec.num_seqs
+        rng = np.random.default_rng(5)
+        qf = rng.standard_normal((S, q_len, Hq, D)).astype(np.float32)
+        q = qf if dtype == "f32" else (qf.view(np.uint32) >> 16).astype(np.uint16)
+        out = oracle.decode_q(q, kc, vc, bt, sl, spec.scale, dtype=dtype, lib=lib)
+        qw = widen(q)
+        G = Hq // Hkv
+        for s_ in range(S):
+            L = int(sl[s_])
+            ref = np.zeros((q_len, Hq, D))
+            if L > 0:
+                k, v = dense_kv(kl, vl, bt, L, s_)
+                mask = torch.ones(q_len, L, dtype=torch.bool).tril(diagonal=L - q_len)
+                kt = torch.from_numpy(np.ascontiguousarray(k)).repeat_interleave(G, dim=0)[None]
+                vt = torch.from_numpy(np.ascontiguousarray(v)).repeat_interleave(G, dim=0)[None]
+                qt = torch.from_numpy(np.ascontiguousarray(qw[s_].transpose(1, 0, 2)))[None]
+                o = torch.nn.functional.scaled_dot_product_attention(
+                    qt, kt, vt, attn_mask=mask, scale=float(np.float64(np.float32(spec.scale))))
+                ref = o[0].numpy().transpose(1, 0, 2)
+                ref = np.where(mask.any(dim=1).numpy()[:, None, None], ref, 0.0)
+            assert np.max(np.abs(out[s_] - ref)) <= 1e-12, f"multi-query {dtype} s={s_} L={L}"
+
+
 ALL_PINS = [pin_single_token, pin_uniform_keys, pin_positional_values, pin_closed_form,
             pin_head_mapping, pin_dense_library, pin_outlier_stability, pin_relabel_and_linearity,
-            pin_partitioned_equals_full, pin_partition_statistics, pin_page_counts]
+            pin_partitioned_equals_full, pin_partition_statistics, pin_page_counts,
+            pin_multi_query_causal]

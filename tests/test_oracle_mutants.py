@@ -20,8 +20,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 MUTANTS = [
     ("gqa_modulo_map", "elem(pb->key_cache, key_index(pb, s, h / G, t, d), pb->dtype);",
      "elem(pb->key_cache, key_index(pb, s, h % pb->num_kv_heads, t, d), pb->dtype);"),
-    ("value_head_map", "elem(pb->value_cache, value_index(pb, s, h / G, t, d), pb->dtype);",
-     "elem(pb->value_cache, value_index(pb, s, h % pb->num_kv_heads, t, d), pb->dtype);"),
+    ("value_head_map", "elem(pb->value_cache, value_index(pb, s, hv / G, t, d), pb->dtype);",
+     "elem(pb->value_cache, value_index(pb, s, hv % pb->num_kv_heads, t, d), pb->dtype);"),
     ("logical_not_physical_block",
      "int32_t phys = pb->block_tables[(size_t)s * pb->max_blocks_per_seq + t / pb->block_size];",
      "int32_t phys = t / pb->block_size; (void)s;"),
@@ -45,8 +45,8 @@ MUTANTS = [
     ("unnormalised_output", "for (int d = 0; d < pb->head_dim; ++d) o[d] /= sum;",
      "for (int d = 0; d < pb->head_dim; ++d) o[d] /= 1.0;"),
     ("query_row_of_kv_head",
-     "size_t qoff = ((size_t)s * pb->num_q_heads + h) * pb->head_dim;",
-     "size_t qoff = ((size_t)s * pb->num_q_heads + h / G) * pb->head_dim;"),
+     "size_t qoff = ((size_t)s * pb->q_len * pb->num_q_heads + h) * pb->head_dim;",
+     "size_t qoff = ((size_t)s * pb->q_len * pb->num_q_heads + h / G) * pb->head_dim;"),
     ("merge_sign", "double wgt = exp(m[p] - gmax) * es[p] / total;",
      "double wgt = exp(gmax - m[p]) * es[p] / total;"),
     ("merge_drops_exp_sum", "double wgt = exp(m[p] - gmax) * es[p] / total;",
@@ -56,6 +56,11 @@ MUTANTS = [
     ("partition_count_floor",
      "long parts = L > 0 ? ((long)L + partition_size - 1) / partition_size : 0;",
      "long parts = L > 0 ? (long)L / partition_size : 0;"),
+    ("causal_off_by_one", "int visible = seq_lens[s] - q_len + j + 1; /* tokens 0 .. L - q_len + j */",
+     "int visible = seq_lens[s] - q_len + j;"),
+    ("query_token_ignored",
+     "size_t qoff = ((size_t)s * pb->q_len * pb->num_q_heads + h) * pb->head_dim;",
+     "size_t qoff = ((size_t)s * pb->q_len * pb->num_q_heads + h % pb->num_q_heads) * pb->head_dim;"),
     ("bf16_widen_wrong_half", "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;",
      "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 15;"),
 ]
