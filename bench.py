@@ -179,8 +179,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--extras", action="store_true",
-                    help="also time V2 at other partition sizes, V2 in a single launch and V1 "
-                         "(same workload)")
+                    help="also time V2 at other partition sizes, V2 in a single launch, V2 with "
+                         "several query tokens per sequence and V1 (same workload)")
     ap.add_argument("--no-extras", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="instead of the step benchmark, time V1 / V2 over a grid of batch shapes "
@@ -333,6 +333,27 @@ def main():
             extras[f"v2_single_launch_p{P}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 50, 2)
         except pa.PagedAttentionError as e:
             extras[f"v2_single_launch_p{P}_us_per_step"] = f"not applicable: {e}"
+        # Several query tokens per sequence (causal over the cache): as many as fit the
+        # 16 tile columns with this GQA group.
+        qlen = max(1, 16 // (Hq // spec.num_kv_heads))
+        if qlen > 1:
+            qm = torch.randn(S, qlen, Hq, D, device=dev).to(q.dtype)
+            om = torch.empty_like(qm)
+            wsq = pa.new_workspace(S, qlen * Hq, D, L, P, device=dev)
+
+            def multi(i):
+                c = i % len(kcs)
+                pa.pa_decode_v2_q(om, qm, kcs[c], vcs[c], bt, sl, spec.scale, L, P, wsq)
+            for i in range(5):
+                multi(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(50):
+                multi(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            extras[f"v2_qlen{qlen}_p{P}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 50, 2)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         step(0, "v1")
         e0.record(stream)

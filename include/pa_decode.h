@@ -63,7 +63,8 @@
  *     never used: any value there, NaN included, does not reach the output.
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_q_heads a multiple
- * of num_kv_heads with group size G <= 16; partition_size a multiple of 16;
+ * of num_kv_heads with group size G <= 16 (G * q_len <= 16 for the q_len entry
+ * points); partition_size a multiple of 16;
  * num_seqs and num_kv_heads <= 65535.  Anything else returns
  * PA_ERR_UNSUPPORTED or PA_ERR_INVALID_SHAPE.
  */
@@ -187,6 +188,38 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                                 int max_blocks_per_seq, int max_seq_len, float scale,
                                 pa_dtype_t dtype, int partition_size, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * Decode of q_len query tokens per sequence (q_len >= 1: several new tokens at
+ * once, as in speculative decoding).  query and out are
+ * [num_seqs][q_len][num_q_heads][head_dim].  The q_len tokens are the last
+ * q_len positions of each sequence and are already in the cache.  Query token j
+ * sits at position L - q_len + j and attends to tokens 0 .. L - q_len + j
+ * (causal over the cache); a token that sees no token (L < q_len - j) gets a
+ * zero row.  This extends the decode step along the q_len dimension that the
+ * pages batch next to the GQA group (commit 490ff98, the summary_statistics
+ * message).  Each (token, head) pair is one column of the kernel's 16-wide
+ * tiles, so (num_q_heads / num_kv_heads) * q_len <= 16, else PA_ERR_UNSUPPORTED.
+ * pa_decode_v1_q is the single pass.  pa_decode_v2_q is split-KV in two
+ * launches; its workspace holds q_len * num_q_heads rows per sequence, i.e.
+ * pa_workspace_size(num_seqs, q_len * num_q_heads, head_dim, max_seq_len,
+ * partition_size) bytes.  With q_len = 1 they equal pa_decode_v1 and
+ * pa_decode_v2 bit for bit.
+ */
+pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype_t dtype, void *stream);
+
+pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype_t dtype, int partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
  * for partitions p < ceil(L / partition_size) of each sequence; other entries

@@ -8,7 +8,7 @@ call raises.
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
 pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_select_v2_auto,
-pa_decode_auto, pa_decode_v2_single, pa_status_string.
+pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_status_string.
 """
 from __future__ import annotations
 
@@ -62,6 +62,11 @@ def load_library():
     lib.pa_decode_auto.restype = I
     lib.pa_decode_v1.argtypes = [P] + common + [P]
     lib.pa_decode_v1.restype = I
+    common_q = common[:6] + [I] + common[6:]  # q_len after num_seqs
+    lib.pa_decode_v1_q.argtypes = [P] + common_q + [P]
+    lib.pa_decode_v1_q.restype = I
+    lib.pa_decode_v2_q.argtypes = [P] + common_q + [I, P, Z, P]
+    lib.pa_decode_v2_q.restype = I
     lib.pa_decode_v2.argtypes = [P] + common + [I, P, Z, P]
     lib.pa_decode_v2.restype = I
     lib.pa_decode_v2_single.argtypes = [P] + common + [I, P, Z, P]
@@ -163,6 +168,17 @@ def _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_s
     return args
 
 
+def _problem_q(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len):
+    """Arguments of the q_len entry points: query [S, q_len, Hq, D]."""
+    if query.dim() != 4:
+        raise ValueError("query must be [S, q_len, Hq, D]")
+    S, q_len, Hq, D = query.shape
+    args = _problem(query.view(S, q_len * Hq, D), key_cache, value_cache, block_tables, seq_lens,
+                    scale, max_seq_len)
+    # replace the flattened head count by (q_len, Hq)
+    return args[:5] + [S, q_len, Hq] + args[7:], q_len, Hq
+
+
 def _check(st, where):
     if st != PA_OK:
         raise PagedAttentionError(st, where)
@@ -233,6 +249,31 @@ def pa_decode_auto(out, query, key_cache, value_cache, block_tables, seq_lens, s
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode_auto(o, *args, int(partition_size), wp, wb, _stream(stream)),
            "pa_decode_auto")
+
+
+def pa_decode_v1_q(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                   stream=None):
+    """V1 for q_len query tokens per sequence: query and out [S, q_len, Hq, D]."""
+    args, _, _ = _problem_q(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                            max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    _check(load_library().pa_decode_v1_q(o, *args, _stream(stream)), "pa_decode_v1_q")
+
+
+def pa_decode_v2_q(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                   partition_size, workspace, stream=None):
+    """V2 for q_len query tokens per sequence; the workspace is sized for S sequences
+    of q_len * Hq heads (new_workspace(S, q_len * Hq, ...))."""
+    args, _, _ = _problem_q(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                            max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2_q(o, *args, int(partition_size), wp, wb, _stream(stream)),
+           "pa_decode_v2_q")
 
 
 def pa_decode_v2_partials(query, key_cache, value_cache, block_tables, seq_lens, scale,

@@ -88,10 +88,10 @@ bool layout(int num_seqs, int num_q_heads, int head_dim, int max_seq_len, int pa
 
 pa_status_t check_problem(const void *query, const void *key_cache, const void *value_cache,
                           const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
-                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                          int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
-                          pa_dtype_t dtype) {
-    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+                          int q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                          float scale, pa_dtype_t dtype) {
+    if (num_seqs < 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seq_len < 0)
         return PA_ERR_INVALID_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_SHAPE;
@@ -101,7 +101,7 @@ pa_status_t check_problem(const void *query, const void *key_cache, const void *
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
-    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if ((long long)(num_q_heads / num_kv_heads) * q_len > kMaxGroup) return PA_ERR_UNSUPPORTED;
     if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!query || !key_cache || !value_cache || !block_tables || !seq_lens)
@@ -113,9 +113,11 @@ pa_status_t check_problem(const void *query, const void *key_cache, const void *
 
 pa::Problem make_problem(const void *query, const void *key_cache, const void *value_cache,
                          const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
-                         int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
-                         int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype) {
+                         int q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                         int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                         pa_dtype_t dtype) {
     pa::Problem pb;
+    pb.qlen = q_len;
     pb.query = query;
     pb.key_cache = key_cache;
     pb.value_cache = value_cache;
@@ -223,20 +225,83 @@ int pa_select_v2(int max_seq_len, int num_seqs, int num_kv_heads, int partition_
     return max_seq_len > kV2MinSeqLen ? 1 : 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
+                      const void *value_cache, const int32_t *block_tables,
+                      const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                      void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!out) return PA_ERR_NULL_POINTER;
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    return from_hip(pa::launch_single_pass(pb, out, static_cast<hipStream_t>(stream)));
+}
+
+// V2 Phase 1 (+ Phase 2 when out != nullptr).  With q_len query tokens per
+// sequence the partials have q_len * num_q_heads rows per sequence.
+pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *key_cache,
+                      const void *value_cache, const int32_t *block_tables,
+                      const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                      int partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    const long long rows_per_seq = (long long)q_len * num_q_heads;
+    if (rows_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    pa::Partials parts;
+    st = carve(num_seqs, (int)rows_per_seq, num_kv_heads, head_dim, max_seq_len, partition_size,
+               workspace, workspace_bytes, &parts);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (want_out && !out) return PA_ERR_NULL_POINTER;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                  q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (parts.max_parts > 0) {
+        st = from_hip(pa::launch_partitions(pb, parts, hs));
+        if (st != PA_OK || !want_out) return st;
+    }
+    if (!want_out) return PA_OK;
+    return from_hip(pa::launch_reduce(seq_lens, num_seqs, (int)rows_per_seq, head_dim,
+                                      max_seq_len, pb.dtype, parts, out, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
 pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
                          const void *value_cache, const int32_t *block_tables,
                          const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                          int max_seq_len, float scale, pa_dtype_t dtype, void *stream) {
-    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                   max_blocks_per_seq, max_seq_len, scale, dtype);
-    if (st != PA_OK || num_seqs == 0) return st;
-    if (!out) return PA_ERR_NULL_POINTER;
-    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
-                                  max_blocks_per_seq, max_seq_len, scale, dtype);
-    return from_hip(pa::launch_single_pass(pb, out, static_cast<hipStream_t>(stream)));
+    return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, 1,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, stream);
+}
+
+pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype_t dtype, void *stream) {
+    return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, q_len,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, stream);
 }
 
 pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
@@ -246,18 +311,10 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                   int max_blocks_per_seq, int max_seq_len, float scale,
                                   pa_dtype_t dtype, int partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream) {
-    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                   max_blocks_per_seq, max_seq_len, scale, dtype);
-    if (st != PA_OK) return st;
-    pa::Partials parts;
-    st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
-               workspace, workspace_bytes, &parts);
-    if (st != PA_OK || num_seqs == 0 || parts.max_parts == 0) return st;
-    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
-                                  max_blocks_per_seq, max_seq_len, scale, dtype);
-    return from_hip(pa::launch_partitions(pb, parts, static_cast<hipStream_t>(stream)));
+    return decode_v2(nullptr, false, query, key_cache, value_cache, block_tables, seq_lens,
+                     num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
+                     workspace_bytes, stream);
 }
 
 pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
@@ -285,25 +342,23 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                          int max_seq_len, float scale, pa_dtype_t dtype, int partition_size,
                          void *workspace, size_t workspace_bytes, void *stream) {
-    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                   max_blocks_per_seq, max_seq_len, scale, dtype);
-    if (st != PA_OK) return st;
-    pa::Partials parts;
-    st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
-               workspace, workspace_bytes, &parts);
-    if (st != PA_OK || num_seqs == 0) return st;
-    if (!out) return PA_ERR_NULL_POINTER;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
-                                  max_blocks_per_seq, max_seq_len, scale, dtype);
-    if (parts.max_parts > 0) {
-        st = from_hip(pa::launch_partitions(pb, parts, hs));
-        if (st != PA_OK) return st;
-    }
-    return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
-                                      pb.dtype, parts, out, hs));
+    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                     1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
+                     workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype_t dtype, int partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                     q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
+                     workspace_bytes, stream);
 }
 
 pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_cache,
@@ -314,7 +369,7 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                                 pa_dtype_t dtype, int partition_size, void *workspace,
                                 size_t workspace_bytes, void *stream) {
     pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                    max_blocks_per_seq, max_seq_len, scale, dtype);
     if (st != PA_OK) return st;
     pa::Partials parts;
@@ -324,7 +379,7 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
     if (!out) return PA_ERR_NULL_POINTER;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
-                                  num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                  1, num_q_heads, num_kv_heads, head_dim, num_blocks,
                                   max_blocks_per_seq, max_seq_len, scale, dtype);
     if (parts.max_parts == 0)  // no tokens anywhere: the reduce alone writes the zero rows
         return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,

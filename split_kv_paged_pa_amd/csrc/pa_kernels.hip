@@ -284,8 +284,8 @@ template <typename T, int D, int NW, int U, int MODE>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int num_kv_heads, int group, int num_blocks, int max_blocks, int max_seq_len, float scale,
-    int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
+    int num_kv_heads, int group, int qlen, int num_blocks, int max_blocks, int max_seq_len,
+    float scale, int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
     float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
     T *__restrict__ out) {
     constexpr bool kFinal = MODE == kSinglePass;
@@ -356,12 +356,19 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     }
     auto part_end = [&](int p) { return min((p + 1) * bp, nblk); };  // end block of partition p
 
-    // Q^T operand: lane (g, grp) holds chunk c of query head kvh*G + g (zero for g >= G).
+    // Columns: column g of the MFMA tiles is (query token g / G, head kvh*G + g % G)
+    // of this sequence, for g < G * qlen (qlen query tokens per sequence; 1 for
+    // plain decode).  Query and output rows are [S][qlen][Hq][D]; the row of column
+    // gg is qrow_of(gg).
     const int g = l16;
+    const int ncol = group * qlen;
+    auto qrow_of = [&](int gg) {
+        return ((size_t)s * qlen + gg / group) * num_q_heads + (size_t)kvh * group + gg % group;
+    };
+    // Q^T operand: lane (g, grp) holds chunk c of column g's query (zero for g >= ncol).
     uint4 qv[NC];
-    if (g < group) {
-        const uint4 *qrow = reinterpret_cast<const uint4 *>(
-            query + ((size_t)s * num_q_heads + (size_t)kvh * group + g) * D);
+    if (g < ncol) {
+        const uint4 *qrow = reinterpret_cast<const uint4 *>(query + qrow_of(g) * D);
 #pragma unroll
         for (int c = 0; c < NC; ++c) qv[c] = qrow[c * 4 + grp];
     } else {
@@ -386,8 +393,10 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     constexpr int kVStep = 16 * kRowBytes;
     const int k_lane = 16 * lane;
     const int v_lane = kRowBytes * l16 + 4 * (int)sizeof(T) * grp;
-    const char *dummy = reinterpret_cast<const char *>(
-        query + ((size_t)s * num_q_heads + (size_t)kvh * group) * D);
+    const char *dummy = reinterpret_cast<const char *>(query + qrow_of(0) * D);
+    // Last token column g may see: token j of qlen sits at L - qlen + j (causal
+    // over the cache); unused columns take L - 1.
+    const int lim = g < ncol ? L - qlen + g / group : L - 1;
 
     // ---- issue side: wave w takes blocks p*bp + w, p*bp + w + NW, ... of each of
     // the workgroup's partitions p in turn; loads run U-1 blocks ahead of the math
@@ -448,13 +457,15 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         float z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            z[r] = (!kTail || 4 * grp + r < valid) ? sacc[r] * scale : -INFINITY;
+            z[r] = (!kTail || j * kBlockTokens + 4 * grp + r <= lim) ? sacc[r] * scale : -INFINITY;
         const float bm = column_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
         // Rescale only when some column's max grew: otherwise the factor is
         // exactly 1 and skipping it changes no bit.
         if (__builtin_amdgcn_ballot_w64(bm > m_run) != 0) {
             const float m_new = fmaxf(m_run, bm);
-            const float alpha = exp_e(m_run - m_new);
+            // A column that has seen nothing yet keeps m = -inf (only in tail blocks with
+            // several query tokens); its factor is 0, not exp(-inf + inf).
+            const float alpha = m_run == -INFINITY ? 0.f : exp_e(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
 #pragma unroll
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         }
         float pr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = exp_e(z[r] - m_run);
+        for (int r = 0; r < 4; ++r) pr[r] = (kTail && z[r] == -INFINITY) ? 0.f : exp_e(z[r] - m_run);
         l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
         if (kTail) {
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         for (int t = 0; t < NT; ++t) M::pv(acc[t], vr[t], pb);
     };
     auto step = [&](int j, const uint4 (&kr)[NC], VU (&vr)[NT]) {
-        if ((j + 1) * kBlockTokens <= L)
+        if ((j + 1) * kBlockTokens <= L - qlen + 1)  // every token visible to every column
             attend(std::false_type{}, j, kr, vr);
         else
             attend(std::true_type{}, j, kr, vr);
@@ -494,7 +505,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4 *>(&sm_o[w][g][16 * t + 4 * grp]) = acc[t];
         __syncthreads();
-        const size_t head0 = (size_t)s * num_q_heads + (size_t)kvh * group;
         // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
         if (threadIdx.x < 16) {
             const int gg = threadIdx.x;
@@ -524,15 +534,15 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 const float inv = total > 0.f ? 1.f / total : 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
-                if (!kFinal && gg < group) {
-                    const size_t row = (head0 + gg) * max_parts + p;
+                if (!kFinal && gg < ncol) {
+                    const size_t row = qrow_of(gg) * max_parts + p;
                     exp_sums[row] = total;
                     max_logits[row] = mx;
                 }
             }
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < group * D; idx += NW * 64) {
+        for (int idx = threadIdx.x; idx < ncol * D; idx += NW * 64) {
             const int gg = idx / D;
             const int d = idx - gg * D;
             float o = 0.f;
@@ -541,9 +551,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             if (MODE == kFused) {
                 sm_ga[gg][d] = sm_ga[gg][d] * sm_gs[gg] + o;  // same thread owns (gg, d) every time
             } else if (kFinal) {
-                out[(head0 + gg) * D + d] = M::from_float(o);
+                out[qrow_of(gg) * D + d] = M::from_float(o);
             } else {
-                tmp_out[((head0 + gg) * max_parts + p) * D + d] = o;
+                tmp_out[(qrow_of(gg) * max_parts + p) * D + d] = o;
             }
         }
         m_run = -INFINITY;
@@ -748,7 +758,7 @@ hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hi
     attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), MODE><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
-        pb.num_kv_heads, group, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
+        pb.num_kv_heads, group, pb.qlen, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
         kFinal ? kBlockTokens : parts->partition_size, ppw, kFinal ? 0 : parts->max_parts,
         kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
         kFinal ? nullptr : parts->max_logits, MODE == kFused ? parts->tickets : nullptr,

@@ -12,12 +12,13 @@ enum class Dtype : int { F32 = 0, BF16 = 1 };
 
 // One decode batch, already validated by the ABI layer.
 struct Problem {
-    const void *query;          // [S][Hq][D]
+    const void *query;          // [S][qlen][Hq][D]
     const void *key_cache;      // [num_blocks][Hkv][D / x][16][x], x = 16 bytes of values
     const void *value_cache;    // [num_blocks][Hkv][D][16]
     const int32_t *block_tables;  // [S][max_blocks]
     const int32_t *seq_lens;    // [S]
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int qlen;                   // query tokens per sequence (query/out are [S][qlen][Hq][D])
     int num_blocks, max_blocks, max_seq_len;
     float scale;
     Dtype dtype;

@@ -340,6 +340,72 @@ def test_decode_auto(lens, hkv, v2):
 
 
 # ---------------------------------------------------------------------------
+# q_len query tokens per sequence (causal over the cache).
+# ---------------------------------------------------------------------------
+MULTI = [  # dtype, D, Hq, Hkv, q_len, P
+    ("bf16", 128, 32, 4, 2, 512),
+    ("bf16", 128, 16, 4, 4, 16),
+    ("f32", 64, 8, 2, 3, 512),
+    ("bf16", 64, 5, 1, 3, 1024),
+    ("bf16", 128, 16, 16, 4, 256),
+]
+MULTI_LENS = [1, 2, 3, 4, 15, 16, 17, 100, 513, 1025, 3000, 0]
+
+
+def _multi_query(spec, q_len, dev="cuda"):
+    rng = np.random.default_rng(spec.seed)
+    qf = rng.standard_normal((spec.num_seqs, q_len, spec.num_q_heads, spec.head_dim),
+                             dtype=np.float32)
+    return torch.from_numpy(qf).to(wl.torch_dtype(spec.dtype)).to(dev)
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,q_len,P", MULTI, ids=lambda x: str(x))
+def test_multi_query_decode(dtype, D, Hq, Hkv, q_len, P):
+    spec = wl.custom("multiq", 121, dtype, Hq, Hkv, D, MULTI_LENS)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q = _multi_query(spec, q_len)
+    print(f"[case] multi-query {dtype} D={D} Hq={Hq} Hkv={Hkv} q_len={q_len} P={P}", flush=True)
+    _, kc, vc, bt, sl = b.numpy()
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype=dtype)
+    out1 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v1_q(out1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len)
+    assert_close(to_f64(out1), ref, dtype, f"v1 q_len={q_len}")
+    ws = pa.new_workspace(spec.num_seqs, q_len * Hq, D, db.max_seq_len, P)
+    ws.fill_(0xFF)
+    out2 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v2_q(out2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len, P, ws)
+    assert_close(to_f64(out2), ref, dtype, f"v2 q_len={q_len} P={P}")
+
+
+def test_multi_query_q1_is_plain_decode():
+    """q_len = 1 through the q_len entry points equals the plain ones bit for bit."""
+    spec = wl.custom("q1", 122, "bf16", 32, 4, 128, [3000, 17, 0, 1024])
+    db = DeviceBatch(wl.generate(spec))
+    q4 = db.query[:, None].contiguous()
+    o1 = torch.empty_like(q4)
+    pa.pa_decode_v1_q(o1, q4, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len)
+    o2 = torch.empty_like(q4)
+    pa.pa_decode_v2_q(o2, q4, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len, 512, db.workspace(512))
+    assert torch.equal(o1[:, 0].view(torch.int16), db.run_v1().view(torch.int16))
+    assert torch.equal(o2[:, 0].view(torch.int16), db.run_v2(512).view(torch.int16))
+
+
+def test_multi_query_too_many_columns():
+    spec = wl.custom("q17", 123, "bf16", 8, 1, 64, [100])
+    db = DeviceBatch(wl.generate(spec))
+    q = _multi_query(spec, 3)  # G * q_len = 24 > 16
+    with pytest.raises(pa.PagedAttentionError) as e:
+        pa.pa_decode_v1_q(torch.empty_like(q), q, db.key_cache, db.value_cache, db.block_tables,
+                          db.seq_lens, spec.scale, db.max_seq_len)
+    assert e.value.status == 3
+
+
+# ---------------------------------------------------------------------------
 # The five named workloads at full size.
 # ---------------------------------------------------------------------------
 FULL = [("tiny_f32_2k", None), ("long_100k_gqa8", None), ("batch16_1k_32k", None),
