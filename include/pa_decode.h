@@ -63,9 +63,9 @@
  *     never used: any value there, NaN included, does not reach the output.
  *
  * Supported shapes: head_dim 64 or 128; block_size 16; num_q_heads a multiple
- * of num_kv_heads with group size G <= 16 (G * q_len <= 16 for the q_len entry
- * points); partition_size a multiple of 16;
- * num_seqs and num_kv_heads <= 65535.  Anything else returns
+ * of num_kv_heads with group size G <= 16; partition_size a multiple of 16;
+ * num_seqs <= 65535 and num_kv_heads * ceil(G * q_len / 16) <= 65535 (q_len = 1
+ * for the plain entry points).  Anything else returns
  * PA_ERR_UNSUPPORTED or PA_ERR_INVALID_SHAPE.
  */
 #ifndef PA_DECODE_H
@@ -199,7 +199,11 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
  * zero row.  This extends the decode step along the q_len dimension that the
  * pages batch next to the GQA group (commit 490ff98, the summary_statistics
  * message).  Each (token, head) pair is one column of the kernel's 16-wide
- * tiles, so (num_q_heads / num_kv_heads) * q_len <= 16, else PA_ERR_UNSUPPORTED.
+ * tiles; a workgroup takes 16 columns of a kv head, so up to
+ * (num_q_heads / num_kv_heads) * q_len = 16 the keys and values are read once,
+ * and beyond that once per 16 columns (a plain paged prefill, correct for any
+ * q_len but not tiled for reuse).  num_kv_heads * ceil(G * q_len / 16) must not
+ * exceed 65535, else PA_ERR_UNSUPPORTED.
  * pa_decode_v1_q is the single pass.  pa_decode_v2_q is split-KV in two
  * launches; its workspace holds q_len * num_q_heads rows per sequence, i.e.
  * pa_workspace_size(num_seqs, q_len * num_q_heads, head_dim, max_seq_len,

@@ -101,8 +101,11 @@ pa_status_t check_problem(const void *query, const void *key_cache, const void *
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
-    if ((long long)(num_q_heads / num_kv_heads) * q_len > kMaxGroup) return PA_ERR_UNSUPPORTED;
-    if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    // 16 (query token, head) columns per workgroup: kv heads * column chunks workgroups in y.
+    const long long chunks = ((long long)(num_q_heads / num_kv_heads) * q_len + 15) / 16;
+    if ((long long)num_kv_heads * chunks > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!query || !key_cache || !value_cache || !block_tables || !seq_lens)
         return PA_ERR_NULL_POINTER;
@@ -261,9 +264,11 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
     if (st != PA_OK) return st;
     const long long rows_per_seq = (long long)q_len * num_q_heads;
     if (rows_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    // Workgroups per (sequence, partition group): kv heads times column chunks.
+    const int chunks = (int)(((long long)(num_q_heads / num_kv_heads) * q_len + 15) / 16);
     pa::Partials parts;
-    st = carve(num_seqs, (int)rows_per_seq, num_kv_heads, head_dim, max_seq_len, partition_size,
-               workspace, workspace_bytes, &parts);
+    st = carve(num_seqs, (int)rows_per_seq, num_kv_heads * chunks, head_dim, max_seq_len,
+               partition_size, workspace, workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (want_out && !out) return PA_ERR_NULL_POINTER;
     hipStream_t hs = static_cast<hipStream_t>(stream);

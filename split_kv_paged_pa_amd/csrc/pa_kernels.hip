@@ -315,7 +315,11 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15;
     const int grp = lane >> 4;
-    const int kvh = blockIdx.y;
+    // blockIdx.y = kv head * column chunks + chunk: the G * qlen (query token, head)
+    // columns of a kv head are taken 16 at a time (one chunk unless G * qlen > 16).
+    const int nchunk = (group * qlen + 15) / 16;
+    const int kvh = blockIdx.y / nchunk;
+    const int c0 = (blockIdx.y - kvh * nchunk) * 16;  // first column of this chunk
     const int s = blockIdx.z;
 
     // The first block this wave will read does not depend on the sequence length:
@@ -356,14 +360,15 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     }
     auto part_end = [&](int p) { return min((p + 1) * bp, nblk); };  // end block of partition p
 
-    // Columns: column g of the MFMA tiles is (query token g / G, head kvh*G + g % G)
-    // of this sequence, for g < G * qlen (qlen query tokens per sequence; 1 for
-    // plain decode).  Query and output rows are [S][qlen][Hq][D]; the row of column
-    // gg is qrow_of(gg).
+    // Columns: column g of the MFMA tiles is global column c = c0 + g, i.e. (query
+    // token c / G, head kvh*G + c % G) of this sequence, for c < G * qlen (qlen query
+    // tokens per sequence; 1 for plain decode).  Query and output rows are
+    // [S][qlen][Hq][D]; the row of column gg is qrow_of(gg).
     const int g = l16;
-    const int ncol = group * qlen;
+    const int ncol = min(16, group * qlen - c0);
     auto qrow_of = [&](int gg) {
-        return ((size_t)s * qlen + gg / group) * num_q_heads + (size_t)kvh * group + gg % group;
+        const int c = c0 + gg;
+        return ((size_t)s * qlen + c / group) * num_q_heads + (size_t)kvh * group + c % group;
     };
     // Q^T operand: lane (g, grp) holds chunk c of column g's query (zero for g >= ncol).
     uint4 qv[NC];
@@ -396,7 +401,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const char *dummy = reinterpret_cast<const char *>(query + qrow_of(0) * D);
     // Last token column g may see: token j of qlen sits at L - qlen + j (causal
     // over the cache); unused columns take L - 1.
-    const int lim = g < ncol ? L - qlen + g / group : L - 1;
+    const int lim = g < ncol ? L - qlen + (c0 + g) / group : L - 1;
+    const int lim_min = L - qlen + c0 / group;  // smallest limit over this chunk's columns
 
     // ---- issue side: wave w takes blocks p*bp + w, p*bp + w + NW, ... of each of
     // the workgroup's partitions p in turn; loads run U-1 blocks ahead of the math
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         for (int t = 0; t < NT; ++t) M::pv(acc[t], vr[t], pb);
     };
     auto step = [&](int j, const uint4 (&kr)[NC], VU (&vr)[NT]) {
-        if ((j + 1) * kBlockTokens <= L - qlen + 1)  // every token visible to every column
+        if ((j + 1) * kBlockTokens <= lim_min + 1)  // every token visible to every column
             attend(std::false_type{}, j, kr, vr);
         else
             attend(std::true_type{}, j, kr, vr);
@@ -754,7 +760,8 @@ hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hi
     constexpr bool kFinal = MODE == kSinglePass;
     const int group = pb.num_q_heads / pb.num_kv_heads;
     const int ppw = kFinal ? 1 : parts->per_group;
-    dim3 grid(kFinal ? 1 : (parts->max_parts + ppw - 1) / ppw, pb.num_kv_heads, pb.num_seqs);
+    const int nchunk = (group * pb.qlen + 15) / 16;  // 16 (query token, head) columns per workgroup
+    dim3 grid(kFinal ? 1 : (parts->max_parts + ppw - 1) / ppw, pb.num_kv_heads * nchunk, pb.num_seqs);
     attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), MODE><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,

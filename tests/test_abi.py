@@ -165,3 +165,13 @@ def test_select_v2_auto_rule():
     import torch
     if not torch.cuda.is_available():
         assert pa.pa_select_v2_auto(4096, 1, 8, 1024) is False
+
+
+def test_multi_query_grid_limit():
+    lib = pa.load_library()
+    # num_kv_heads * ceil(G * q_len / 16) workgroups in grid y: 8 * ceil(8 * 131072 / 16) > 65535.
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 131072, 64, 8, 128, 16, 100, 16384, 262144,
+            0.088, 1, None)
+    assert lib.pa_decode_v1_q(*args) == UNSUP
+    assert lib.pa_decode_v1_q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 64, 8, 128, 16, 100, 16384,
+                              262144, 0.088, 1, None) == SHAPE  # q_len 0

@@ -395,14 +395,32 @@ def test_multi_query_q1_is_plain_decode():
     assert torch.equal(o2[:, 0].view(torch.int16), db.run_v2(512).view(torch.int16))
 
 
-def test_multi_query_too_many_columns():
-    spec = wl.custom("q17", 123, "bf16", 8, 1, 64, [100])
-    db = DeviceBatch(wl.generate(spec))
-    q = _multi_query(spec, 3)  # G * q_len = 24 > 16
-    with pytest.raises(pa.PagedAttentionError) as e:
-        pa.pa_decode_v1_q(torch.empty_like(q), q, db.key_cache, db.value_cache, db.block_tables,
-                          db.seq_lens, spec.scale, db.max_seq_len)
-    assert e.value.status == 3
+CHUNKED = [  # name, Hq, Hkv, q_len, lens, P: more than 16 (token, head) columns per kv head
+    ("g8_q3", 16, 2, 3, [1, 2, 40, 1000, 0], 256),
+    ("g4_q9", 8, 2, 9, [5, 9, 10, 700, 2000], 512),
+    ("prefill_q64", 8, 2, 64, [64, 100, 300, 0, 17], 128),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,q_len,lens,P", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_multi_query_column_chunks(name, Hq, Hkv, q_len, lens, P):
+    """G * q_len > 16: workgroups take 16 columns each (2, 3 and 16 chunks here)."""
+    spec = wl.custom(name, 123, "bf16", Hq, Hkv, 128, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q = _multi_query(spec, q_len)
+    print(f"[case] column chunks {name}", flush=True)
+    _, kc, vc, bt, sl = b.numpy()
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype="bf16")
+    out1 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v1_q(out1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len)
+    assert_close(to_f64(out1), ref, "bf16", f"v1 {name}")
+    ws = pa.new_workspace(spec.num_seqs, q_len * Hq, 128, db.max_seq_len, P)
+    out2 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v2_q(out2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len, P, ws)
+    assert_close(to_f64(out2), ref, "bf16", f"v2 {name}")
 
 
 # ---------------------------------------------------------------------------
