@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -41,8 +42,13 @@ KERNEL_SRC = os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", "pa_kernels.hip
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and whitespace removed: it changes
+    with the code, not with its comments."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return hashlib.sha256("".join(src.split()).encode()).hexdigest()[:16]
 
 
 def phase1_bytes(spec, P):

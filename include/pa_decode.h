@@ -85,7 +85,7 @@ typedef enum {
     PA_ERR_UNSUPPORTED = 3,        /* valid, but outside the supported shapes */
     PA_ERR_WORKSPACE_TOO_SMALL = 4,
     PA_ERR_HIP = 5,                /* a HIP launch failed */
-    PA_ERR_INVALID_ARGUMENT = 6    /* non-finite or non-positive scale, bad enum */
+    PA_ERR_INVALID_ARGUMENT = 6    /* non-finite scale, bad dtype, misaligned pointer */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;

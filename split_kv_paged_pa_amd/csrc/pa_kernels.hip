@@ -1,4 +1,5 @@
-// pa_kernels.hip -- gfx950 (CDNA4) kernels for paged single-query decode attention.
+// pa_kernels.hip -- gfx950 (CDNA4) kernels for paged decode attention (one query
+// token per sequence, or a few: q_len).
 //
 // Method (project_6 commit pages):
 //   - commit 15ef28e (paged_attention_v2_pytorch.py), "[OPT] PagedAttention V2
@@ -11,34 +12,43 @@
 //   - commit 490ff98 (paged_attn.py), the summary_statistics message: the
 //     running state {max, exp-sum, output} of online softmax and its merge
 //     with the factor exp(old max - new max); kv heads are independent and the
-//     query heads of one group are processed together.
+//     query heads of one group (and the q_len query tokens) are processed
+//     together.
 //   - commit 15ef28e, "[OPT] Vectorize paged_attention_v2": keys and values are
 //     fetched through the per-sequence block id list, 16 tokens per block, and
 //     each kv head is broadcast over its query-head group.
 //
 // Design for gfx950 (what differs from the pages' PyTorch design):
-//   - One workgroup of NW wave64s per (partition, kv head, sequence).  All G
-//     query heads of the group sit in the N dimension of one 16x16 MFMA tile,
-//     so every key/value block is read from HBM once for the whole group.
+//   - One workgroup of NW wave64s per (partition group, kv head, sequence).  The
+//     G query heads of the group -- times the q_len query tokens -- are the N
+//     dimension (columns) of 16x16 MFMA tiles, so every key/value block is read
+//     from HBM once for all of them; past 16 columns, grid y also counts column
+//     chunks of 16.  When partitions are few, one workgroup takes several
+//     consecutive partitions and streams across their boundaries.
 //   - A wave owns whole 16-token blocks (blocks j = first + w, first + w + NW, ...).
 //     The caches use the split layout (keys [D/x][16][x], values [D][16] per
 //     block and kv head, x = 16 bytes of values), so every load instruction of
 //     a wave reads contiguous memory: key chunk c of lane l is the 16 bytes at
 //     1024*c + 16*l of the slab (token l % 16, d group 4c + l / 16), and value
 //     tile T of lane (i, grp) is the 4 tokens 4*grp .. 4*grp+3 of row d = 16T + i.
+//     Loads run ahead of the math in a ring of register slots with exact waits.
 //   - QK^T: MFMA with A = keys (rows = tokens), B = Q^T (cols = heads).  The
 //     result tile holds, in lane (g, grp) register i, the logit of token
-//     4*grp + i for head g -- exactly the B-operand layout P^T needs for PV,
+//     4*grp + i for column g -- exactly the B-operand layout P^T needs for PV,
 //     so the softmax weights never leave their lane.
 //   - PV as O^T = V^T P^T: the value registers as loaded are the A operand (row
 //     d, four consecutive tokens per lane), so no transpose is needed and the
 //     block loop touches no LDS.
-//   - Masked tokens (past the sequence end) get logit -inf and their value
-//     registers are zeroed before any MFMA touches them, so stale or NaN cache
-//     slots cannot leak through 0 * NaN.
+//   - Masked tokens (past the sequence end, or past a column's causal limit
+//     when q_len > 1) get logit -inf; value slots past the sequence end are
+//     zeroed before any MFMA touches them, so stale or NaN cache slots cannot
+//     leak through 0 * NaN.
 //   - Exponentials: exp(x) = 2^(x log2 e) on v_exp_f32.
-//   - Waves merge their {max, exp-sum, output} states once, through LDS, in a
-//     fixed order: results are bitwise reproducible run to run (no atomics).
+//   - Waves merge their {max, exp-sum, output} states once per partition,
+//     through LDS, in a fixed order, and Phase 2 merges partitions in a fixed
+//     order: results are bitwise reproducible run to run.  The single-launch
+//     form adds one atomic ticket per (sequence, kv head) to find the workgroup
+//     that merges, which then merges in a fixed order too.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
