@@ -69,6 +69,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// Store written through to the device's point of coherence (a device-scope
+// relaxed atomic store: global_store ... sc1).  Used for the partials, which the
+// next kernel reads: leaving no dirty lines in the L2s shortens the end of the
+// kernel (measured: 0.4-0.5 us per Phase-1 launch).
+__device__ __forceinline__ void store_through(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // max over lanes l, l^16, l^32, l^48 (the four rows of a column), on the
 // gfx950 permlane swaps: permlane32_swap(v, v) returns {v[l % 32], v[l % 32 + 32]}
 // and permlane16_swap(v, v) returns the two rows of each row pair.
@@ -552,8 +560,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
                 if (!kFinal && gg < ncol) {
                     const size_t row = qrow_of(gg) * max_parts + p;
-                    exp_sums[row] = total;
-                    max_logits[row] = mx;
+                    store_through(exp_sums + row, total);
+                    store_through(max_logits + row, mx);
                 }
             }
         }
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             } else if (kFinal) {
                 out[qrow_of(gg) * D + d] = M::from_float(o);
             } else {
-                tmp_out[(qrow_of(gg) * max_parts + p) * D + d] = o;
+                store_through(tmp_out + (qrow_of(gg) * max_parts + p) * D + d, o);
             }
         }
         m_run = -INFINITY;
