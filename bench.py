@@ -38,14 +38,18 @@ from split_kv_paged_pa_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "KV GB/s read and % of HBM peak; decode-attn µs/step at 100K ctx, GQA 8"
-KERNEL_SRC = os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", "pa_kernels.hip")
+# Sources of the decode kernels (the Phase-1 kernel whose traffic profiles/ records).
+KERNEL_SRC = [os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", f)
+              for f in ("pa_kernels.hip", "pa_device.h")]
 
 
 def kernel_sha():
-    """Hash of the kernel source with comments and whitespace removed: it changes
+    """Hash of the kernel sources with comments and whitespace removed: it changes
     with the code, not with its comments."""
-    with open(KERNEL_SRC) as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SRC:
+        with open(path) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     return hashlib.sha256("".join(src.split()).encode()).hexdigest()[:16]

@@ -85,7 +85,8 @@ typedef enum {
     PA_ERR_UNSUPPORTED = 3,        /* valid, but outside the supported shapes */
     PA_ERR_WORKSPACE_TOO_SMALL = 4,
     PA_ERR_HIP = 5,                /* a HIP launch failed */
-    PA_ERR_INVALID_ARGUMENT = 6    /* non-finite scale, bad dtype, misaligned pointer */
+    PA_ERR_INVALID_ARGUMENT = 6    /* non-finite scale, bad dtype, misaligned pointer,
+                                      column_tiles not 0, 1, 2 or 4 */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
@@ -224,6 +225,41 @@ pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
                            int max_blocks_per_seq, int max_seq_len, float scale,
                            pa_dtype_t dtype, int partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Tiled prefill: the same computation as pa_decode_v1_q / pa_decode_v2_q (same
+ * arguments, layouts, workspace and causal rule: query j of q_len sees cache
+ * tokens 0 .. L - q_len + j), on a kernel built for many (query token, head)
+ * columns per kv head, i.e. prefill-like q_len (the [kv_h, gqa, q_len, tile]
+ * batching of commit 490ff98, paged_attn.py, taken to long q_len; partition
+ * partials and their merge as in commit 15ef28e, "[OPT] PagedAttention V2
+ * implementation").  Each wave holds column_tiles tiles of 16 columns and reads
+ * every key/value block of its range once for all of them, so the cache is
+ * re-read once per 64 * column_tiles columns instead of once per 16.
+ *   column_tiles: 1, 2 or 4; 0 lets the library choose.  Other values give
+ *                 PA_ERR_INVALID_ARGUMENT.
+ *   dtype:        PA_DTYPE_BF16 only (PA_ERR_UNSUPPORTED for fp32).
+ * pa_prefill_v1 makes one pass per sequence; pa_prefill_v2 writes one partial
+ * per partition of partition_size tokens into the workspace (sized as for
+ * pa_decode_v2_q) and merges them.  Results agree with the _q entry points to
+ * rounding, not bit for bit: weights are taken against a running reference
+ * max that moves in steps (kept below 2^8 relative to it), which changes the
+ * rounding, not the value.
+ */
+pa_status_t pa_prefill_v1(void *out, const void *query, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                          int column_tiles, void *stream);
+
+pa_status_t pa_prefill_v2(void *out, const void *query, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                          int partition_size, void *workspace, size_t workspace_bytes,
+                          int column_tiles, void *stream);
 
 /* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
  * for partitions p < ceil(L / partition_size) of each sequence; other entries

@@ -8,7 +8,8 @@ call raises.
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
 pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_select_v2_auto,
-pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_status_string.
+pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_prefill_v1,
+pa_prefill_v2, pa_status_string.
 """
 from __future__ import annotations
 
@@ -67,6 +68,10 @@ def load_library():
     lib.pa_decode_v1_q.restype = I
     lib.pa_decode_v2_q.argtypes = [P] + common_q + [I, P, Z, P]
     lib.pa_decode_v2_q.restype = I
+    lib.pa_prefill_v1.argtypes = [P] + common_q + [I, P]
+    lib.pa_prefill_v1.restype = I
+    lib.pa_prefill_v2.argtypes = [P] + common_q + [I, P, Z, I, P]
+    lib.pa_prefill_v2.restype = I
     lib.pa_decode_v2.argtypes = [P] + common + [I, P, Z, P]
     lib.pa_decode_v2.restype = I
     lib.pa_decode_v2_single.argtypes = [P] + common + [I, P, Z, P]
@@ -274,6 +279,32 @@ def pa_decode_v2_q(out, query, key_cache, value_cache, block_tables, seq_lens, s
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode_v2_q(o, *args, int(partition_size), wp, wb, _stream(stream)),
            "pa_decode_v2_q")
+
+
+def pa_prefill_v1(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                  column_tiles=0, stream=None):
+    """Tiled prefill, one pass: query and out [S, q_len, Hq, D], bf16; column_tiles
+    1, 2 or 4 tiles of 16 columns per wave (0: the library's choice)."""
+    args, _, _ = _problem_q(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                            max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    _check(load_library().pa_prefill_v1(o, *args, int(column_tiles), _stream(stream)),
+           "pa_prefill_v1")
+
+
+def pa_prefill_v2(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                  partition_size, workspace, column_tiles=0, stream=None):
+    """Tiled prefill, split-KV: as pa_decode_v2_q (same workspace) plus column_tiles."""
+    args, _, _ = _problem_q(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                            max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_prefill_v2(o, *args, int(partition_size), wp, wb, int(column_tiles),
+                                        _stream(stream)), "pa_prefill_v2")
 
 
 def pa_decode_v2_partials(query, key_cache, value_cache, block_tables, seq_lens, scale,

@@ -3,10 +3,12 @@ bandwidth probe libpa_probe.so in-tree.
 
     python split_kv_paged_pa_amd/build.py [-v]
 
-hipcc flags: gfx950 only, -O3, MFMA results kept in ordinary VGPRs (no
-AGPR copies around the VALU softmax code), and packed-FP32 instructions disabled
+hipcc flags: gfx950 only, -O3, and packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops) so that the compiler never
-emits v_pk_{add,mul,fma}_f32.
+emits v_pk_{add,mul,fma}_f32.  The decode kernels keep MFMA results in ordinary
+VGPRs (no AGPR copies around the VALU softmax code); the prefill kernel, whose
+accumulators outgrow the VGPRs, lets the compiler place them in AGPRs.  Each
+source is compiled to its own object, then linked.
 """
 import os
 import subprocess
@@ -15,23 +17,37 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa_decode.so")
-SOURCES = [os.path.join(CSRC, "pa_kernels.hip"), os.path.join(CSRC, "pa_api.cpp")]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# (source, flags of its own)
+SOURCES = [(os.path.join(CSRC, "pa_kernels.hip"), VGPR_FORM),
+           (os.path.join(CSRC, "pa_prefill.hip"), []),
+           (os.path.join(CSRC, "pa_api.cpp"), [])]
 PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
-PROBE_SOURCES = [os.path.join(CSRC, "pa_probe.hip")]
+PROBE_SOURCES = [(os.path.join(CSRC, "pa_probe.hip"), VGPR_FORM)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+OBJ_DIR = os.path.join(HERE, "_build")
 
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
-         "-Wall", "-Wno-unused-function", "-Wl,--no-undefined"]
+         "-Wall", "-Wno-unused-function"]
 
 
-def _link(sources, lib, verbose, extra):
-    tmp = lib + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", *sources, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+
+
+def _link(sources, lib, verbose, extra):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = []
+    for src, own in sources:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        _run([HIPCC, *FLAGS, *own, *extra, "-x", "hip", "-c", src, "-o", obj], verbose)
+        objs.append(obj)
+    tmp = lib + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+          "-o", tmp], verbose)
     os.replace(tmp, lib)
 
 

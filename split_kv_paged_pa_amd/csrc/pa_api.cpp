@@ -164,6 +164,16 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// tiles: 0 = decode kernel; 1, 2 or 4 = prefill kernel (bf16 only).
+pa_status_t check_tiles(int tiles, pa_dtype_t dtype) {
+    if (tiles == 0) return PA_OK;
+    if (tiles != 1 && tiles != 2 && tiles != 4) return PA_ERR_INVALID_ARGUMENT;
+    return dtype == PA_DTYPE_BF16 ? PA_OK : PA_ERR_UNSUPPORTED;
+}
+
+// Column tiles per wave when the caller leaves the choice to the library.
+int default_tiles(int head_dim) { return head_dim == 64 ? 4 : 2; }
+
 // The single launch applies when every (sequence, kv head) has a counter slot
 // and the last workgroup's merge fits its weight table.
 bool fused_fits(int num_seqs, int num_q_heads, int num_kv_heads, const pa::Partials &parts) {
@@ -237,30 +247,37 @@ pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
                       const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
                       int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
-                      void *stream) {
+                      int tiles, void *stream) {
     pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                    q_len, num_q_heads, num_kv_heads, head_dim, block_size,
                                    num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    st = check_tiles(tiles, dtype);
     if (st != PA_OK || num_seqs == 0) return st;
     if (!out) return PA_ERR_NULL_POINTER;
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
                                   max_blocks_per_seq, max_seq_len, scale, dtype);
-    return from_hip(pa::launch_single_pass(pb, out, static_cast<hipStream_t>(stream)));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (tiles > 0) return from_hip(pa::launch_prefill(pb, nullptr, out, tiles, hs));
+    return from_hip(pa::launch_single_pass(pb, out, hs));
 }
 
 // V2 Phase 1 (+ Phase 2 when out != nullptr).  With q_len query tokens per
-// sequence the partials have q_len * num_q_heads rows per sequence.
+// sequence the partials have q_len * num_q_heads rows per sequence.  tiles > 0:
+// Phase 1 on the prefill kernel with that many column tiles per wave.
 pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *key_cache,
                       const void *value_cache, const int32_t *block_tables,
                       const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
                       int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
-                      int partition_size, void *workspace, size_t workspace_bytes,
+                      int partition_size, void *workspace, size_t workspace_bytes, int tiles,
                       void *stream) {
     pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                    q_len, num_q_heads, num_kv_heads, head_dim, block_size,
                                    num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    st = check_tiles(tiles, dtype);
     if (st != PA_OK) return st;
     const long long rows_per_seq = (long long)q_len * num_q_heads;
     if (rows_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
@@ -276,7 +293,8 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
                                   max_blocks_per_seq, max_seq_len, scale, dtype);
     if (parts.max_parts > 0) {
-        st = from_hip(pa::launch_partitions(pb, parts, hs));
+        st = from_hip(tiles > 0 ? pa::launch_prefill(pb, &parts, nullptr, tiles, hs)
+                                : pa::launch_partitions(pb, parts, hs));
         if (st != PA_OK || !want_out) return st;
     }
     if (!want_out) return PA_OK;
@@ -295,7 +313,7 @@ pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
                          int max_seq_len, float scale, pa_dtype_t dtype, void *stream) {
     return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, 1,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                     max_blocks_per_seq, max_seq_len, scale, dtype, stream);
+                     max_blocks_per_seq, max_seq_len, scale, dtype, 0, stream);
 }
 
 pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
@@ -306,7 +324,7 @@ pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
                            pa_dtype_t dtype, void *stream) {
     return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, q_len,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                     max_blocks_per_seq, max_seq_len, scale, dtype, stream);
+                     max_blocks_per_seq, max_seq_len, scale, dtype, 0, stream);
 }
 
 pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
@@ -319,7 +337,7 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
     return decode_v2(nullptr, false, query, key_cache, value_cache, block_tables, seq_lens,
                      num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, 0, stream);
 }
 
 pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
@@ -350,7 +368,7 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
     return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                      1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, 0, stream);
 }
 
 pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
@@ -363,7 +381,7 @@ pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
     return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                      q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, 0, stream);
 }
 
 pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_cache,
@@ -391,6 +409,32 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                                           pb.dtype, parts, out, hs));
     if (!fused_fits(num_seqs, num_q_heads, num_kv_heads, parts)) return PA_ERR_UNSUPPORTED;
     return from_hip(pa::launch_fused(pb, parts, out, hs));
+}
+
+pa_status_t pa_prefill_v1(void *out, const void *query, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                          int column_tiles, void *stream) {
+    if (column_tiles == 0) column_tiles = default_tiles(head_dim);
+    return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, q_len,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, column_tiles, stream);
+}
+
+pa_status_t pa_prefill_v2(void *out, const void *query, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
+                          int partition_size, void *workspace, size_t workspace_bytes,
+                          int column_tiles, void *stream) {
+    if (column_tiles == 0) column_tiles = default_tiles(head_dim);
+    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                     q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
+                     workspace_bytes, column_tiles, stream);
 }
 
 int pa_select_v2_auto(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {

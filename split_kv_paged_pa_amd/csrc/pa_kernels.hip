@@ -55,66 +55,11 @@
 
 #include <type_traits>
 
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kBlockTokens = 16;
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-
-// Store written through to the device's point of coherence (a device-scope
-// relaxed atomic store: global_store ... sc1).  Used for the partials, which the
-// next kernel reads: leaving no dirty lines in the L2s shortens the end of the
-// kernel (measured: 0.4-0.5 us per Phase-1 launch).
-__device__ __forceinline__ void store_through(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// max over lanes l, l^16, l^32, l^48 (the four rows of a column), on the
-// gfx950 permlane swaps: permlane32_swap(v, v) returns {v[l % 32], v[l % 32 + 32]}
-// and permlane16_swap(v, v) returns the two rows of each row pair.
-__device__ __forceinline__ float column_max(float v) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float column_sum(float v) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// float -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even, two per instruction).
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-    const bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ s16x4 pack_bf16(float a, float b, float c, float d) {
-    return __builtin_bit_cast(s16x4, u32x2{pack2_bf16(a, b), pack2_bf16(c, d)});
-}
-
-__device__ __forceinline__ s16x4 pack_bf16(f32x4 v) { return pack_bf16(v[0], v[1], v[2], v[3]); }
-
-__device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.x, v.y}); }
-__device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
 
 // ---------------------------------------------------------------------------
 // Element-type specific MFMA steps.

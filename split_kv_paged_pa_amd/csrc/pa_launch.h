@@ -46,6 +46,14 @@ hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hip
 int fused_merge_capacity();
 // n uint32 zeros at p (a plain fill kernel).
 hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t stream);
+// Many columns (G * qlen (query token, head) pairs per kv head), bf16 only: waves
+// of nct tiles of 16 columns each stream the blocks themselves.  parts == nullptr:
+// one pass over each sequence -> out; otherwise one workgroup per partition ->
+// partials (then launch_reduce).  nct is 1, 2 or 4.
+hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, int nct,
+                          hipStream_t stream);
+// Workgroups per kv head in grid y of launch_prefill.
+int prefill_column_groups(int group, int qlen, int nct);
 // V2 Phase 2: one workgroup per (query head, sequence): partials -> out.
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
                          int max_seq_len, Dtype dtype, const Partials &parts, void *out,

@@ -1,0 +1,356 @@
+// pa_prefill.hip -- gfx950 (CDNA4) kernel for many query columns per kv head:
+// q_len query tokens per sequence against the paged cache (prefill-like), bf16.
+//
+// Method (project_6 commit pages): the same attention as the decode kernels --
+// per (sequence, query head, query token) the softmax over the visible cache
+// tokens of scale * q.k, applied to the values; kv heads are independent and
+// the G query heads of a group, times the q_len query tokens, share one key /
+// value stream (commit 490ff98, paged_attn.py, the [kv_h, gqa, q_len, tile]
+// batching); the running {max, exp-sum, output} state of online softmax and its
+// rescale by exp(old max - new max) (same message).  Split-KV (commit 15ef28e,
+// "[OPT] PagedAttention V2 implementation"): each partition of P cache tokens
+// writes {normalised output, exp-sum, max logit} and the reduce kernel merges
+// the partitions.  Query j of q_len sees cache tokens 0 .. L - q_len + j.
+//
+// Design for gfx950:
+//   - The decode kernel gives a wave 16 (query token, head) columns and splits
+//     the blocks of a partition over the waves; with many columns that makes
+//     every wave fetch a whole K/V block for only 16 columns of MFMA work, and
+//     the per-CU vector cache bandwidth, not the matrix cores, sets the speed.
+//     Here a wave owns NCT tiles of 16 columns (Q^T held in registers) and
+//     streams every block of its partition itself: each K/V operand loaded
+//     feeds NCT tiles.  The 4 waves of a workgroup take consecutive column
+//     groups of the same kv head and partition, so they read the same blocks
+//     close together in time and the cache serves three of the four.
+//   - MFMA v_mfma_f32_16x16x32_bf16 over steps of 32 tokens (two blocks).
+//     QK^T: A = keys (16 token rows x 32 d), B = Q^T (32 d x 16 columns).  The
+//     two 16-token tiles of a step take the tokens in an interleaved order --
+//     tile T row r is token 16*(r/8) + 8*((r/4)%2) + 4T + r%4 of the step -- so
+//     that lane (n, q) ends up holding the logits of tokens 8q .. 8q+7 of column
+//     n: exactly the B operand P^T of the PV MFMA (k slot 8q+e = token 8q+e).
+//   - PV as O^T = V^T P^T: with values stored [D][16] per block, the A operand
+//     of lane (n, q) -- row d = 16t + n, tokens 8q .. 8q+7 -- is one contiguous
+//     16-byte load; keys, stored [D/8][16][8], are 16-byte loads as well.
+//   - Online softmax in base 2 with a lazy reference: the weights are
+//     2^(z log2 e - m) with m the column's reference max, which moves only when
+//     a logit exceeds it by more than 2^8 (then the output and exp-sum are
+//     rescaled); weights stay below 256, the ratio output / exp-sum is what is
+//     kept, and the true max is tracked on the side for the partials.
+//   - The accumulators are the MFMA result registers (AGPRs when the register
+//     file needs them: this file is built without forcing VGPR results).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kPrefillWaves = 4;
+// A column's reference max moves when a logit exceeds it by more than this (log2 units).
+constexpr float kLazyLog2 = 8.f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma_bf16_32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The first `keep` (0..8) bf16 values of v, the rest zeroed.
+__device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
+    auto word = [&](uint32_t x, int k) -> uint32_t {
+        return keep >= k + 2 ? x : (keep == k + 1 ? (x & 0x0000ffffu) : 0u);
+    };
+    return make_uint4(word(v.x, 0), word(v.y, 2), word(v.z, 4), word(v.w, 6));
+}
+
+// Grid: x = partition (0 for the single pass), y = kv head * column groups of
+// kPrefillWaves * 16 * NCT columns, z = sequence.  Wave w of a workgroup owns
+// columns cw .. cw + 16*NCT - 1; column c is (query token c / G, head kvh*G + c % G).
+// kFinal: one pass over the whole sequence, output written.  Otherwise partition
+// blockIdx.x of P tokens, partials written: tmp_out[row][p][D] (normalised
+// output), exp_sums[row][p] (sum of exp(z - max)), max_logits[row][p] (max of z),
+// with row = (s * q_len + token) * Hq + head and z = scale * q.k; a column that
+// sees no token of the partition writes {0, 0, -inf}.
+template <int D, int NCT, bool kFinal>
+__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
+    const uint16_t *__restrict__ query, const uint16_t *__restrict__ key_cache,
+    const uint16_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ seq_lens, int num_q_heads, int num_kv_heads, int group, int qlen,
+    int num_blocks, int max_blocks, int max_seq_len, float scale, int partition_size,
+    int max_parts, float *__restrict__ tmp_out, float *__restrict__ exp_sums,
+    float *__restrict__ max_logits, uint16_t *__restrict__ out) {
+    constexpr int KS = D / 32;       // 32-wide steps over d (QK^T)
+    constexpr int DT = D / 16;       // 16-row d tiles of the output
+    constexpr int WCOLS = 16 * NCT;  // columns per wave
+    constexpr int NW = kPrefillWaves;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;  // column of a tile; row of the A operands
+    const int q = lane >> 4;  // lane group: k slots 8q .. 8q+7, result rows 4q .. 4q+3
+
+    const int ncols = group * qlen;
+    const int ygroups = (ncols + NW * WCOLS - 1) / (NW * WCOLS);
+    const int kvh = blockIdx.y / ygroups;
+    const int cw = ((blockIdx.y - kvh * ygroups) * NW + w) * WCOLS;  // first column of the wave
+    if (cw >= ncols) return;  // no barrier in this kernel: a wave without columns just leaves
+    const int s = blockIdx.z;
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    int p = 0, jb = 0, je = nblk;  // blocks [jb, je) of this partition
+    if (!kFinal) {
+        const int bp = partition_size / kBlockTokens;
+        p = blockIdx.x;
+        if (p >= (nblk + bp - 1) / bp) return;  // past the sequence: never read
+        jb = p * bp;
+        je = min(jb + bp, nblk);
+    }
+
+    // Columns of this lane: cw + 16 ct + n.  lim: the last cache token the column
+    // sees (L - 1 for a column past the end, whose results are never stored).
+    auto qrow_of = [&](int c) {  // query / output row of column c
+        const int tok = c / group;
+        return ((size_t)s * qlen + tok) * num_q_heads + (size_t)kvh * group + (c - tok * group);
+    };
+    // The maxima are taken over the raw products q.k and scaled afterwards, which
+    // needs a positive factor: a negative scale flips the sign bits of the bf16
+    // query instead (exact), and a zero scale becomes a tiny positive one (all
+    // weights still round to 1).
+    const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+    const float c2 = fmaxf(fabsf(scale) * kLog2e, 1e-30f);  // |q.k| -> logit in log2 units
+    int lim[NCT];
+    uint4 qv[NCT][KS];  // Q^T operand: d = 32 ks + 8q .. +7 of the column's query row
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = cw + 16 * ct + n;
+        lim[ct] = c < ncols ? L - qlen + c / group : L - 1;
+        const uint4 *src = reinterpret_cast<const uint4 *>(query + qrow_of(c) * D) + q;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 v = c < ncols ? src[4 * ks] : make_uint4(0, 0, 0, 0);
+            qv[ct][ks] = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+        }
+    }
+    const int c_last = min(cw + WCOLS, ncols) - 1;
+    const int lim_lo = L - qlen + cw / group;      // smallest limit of the wave's columns
+    const int lim_hi = L - qlen + c_last / group;  // largest
+    // Blocks past lim_hi are invisible to every column of the wave.
+    const int je_w = lim_hi < 0 ? jb : max(jb, min(je, lim_hi / kBlockTokens + 1));
+
+    float m[NCT], mt[NCT], l[NCT];    // reference max, true max (log2 units), lane's exp-sum share
+    f32x4 acc[NCT][DT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        m[ct] = -INFINITY;
+        mt[ct] = -INFINITY;
+        l[ct] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Byte offsets in a (block, kv head) slab.  Keys [D/8][16][8]: A row n of tile
+    // T is token 8*((n/4)%2) + 4T + n%4 of block n/8 (of the step's two), d chunk
+    // 4 ks + q.  Values [D][16]: lane (n, q) reads row d = 16t + n, tokens
+    // 8*(q%2) .. +7 of block q/2.
+    constexpr int kSlabBytes = kBlockTokens * D * 2;
+    const int k_blk = n >> 3;
+    const int k_off = q * 256 + (8 * ((n >> 2) & 1) + (n & 3)) * 16;
+    const int v_blk = q >> 1;
+    const int v_off = n * 32 + (q & 1) * 16;
+    const int32_t *bt = block_tables + (size_t)s * max_blocks;
+    const char *kbase = reinterpret_cast<const char *>(key_cache) + (size_t)kvh * kSlabBytes;
+    const char *vbase = reinterpret_cast<const char *>(value_cache) + (size_t)kvh * kSlabBytes;
+    const size_t blk_stride = (size_t)num_kv_heads * kSlabBytes;
+    // Loads of a block that is not attended read the first 16 bytes of the
+    // wave's first query row instead, so every step issues the same loads.
+    const char *dummy = reinterpret_cast<const char *>(query + qrow_of(cw) * D);
+
+    // Block ids of the step at block j (blocks j, j + 1); -1: not attended.
+    auto ids = [&](int j, int &id0, int &id1) {
+        id0 = j < je_w ? bt[j] : -1;
+        id1 = j + 1 < je_w ? bt[j + 1] : -1;
+        if ((unsigned)id0 >= (unsigned)num_blocks) id0 = -1;
+        if ((unsigned)id1 >= (unsigned)num_blocks) id1 = -1;
+    };
+    auto load_k = [&](int id0, int id1, uint4 (&kr)[2][KS]) {
+        const bool kok = (k_blk ? id1 : id0) >= 0;
+        const char *kp = kok ? kbase + (size_t)(k_blk ? id1 : id0) * blk_stride + k_off : dummy;
+        const int kstep = kok ? 1024 : 0, ktile = kok ? 64 : 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kr[t][ks] = *reinterpret_cast<const uint4 *>(kp + ks * kstep + t * ktile);
+    };
+    auto load_v = [&](int id0, int id1, uint4 (&vr)[DT]) {
+        const bool vok = (v_blk ? id1 : id0) >= 0;
+        const char *vp = vok ? vbase + (size_t)(v_blk ? id1 : id0) * blk_stride + v_off : dummy;
+        const int vstep = vok ? 512 : 0;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vr[t] = *reinterpret_cast<const uint4 *>(vp + t * vstep);
+    };
+
+    // One step of 32 tokens: logits, reference update, weights, PV.
+    auto step = [&](int j, const uint4 (&kr)[2][KS], uint4 (&vr)[DT], bool ok0, bool ok1) {
+        const int t0 = j * kBlockTokens + 8 * q;  // lane's first token: t0 + 4T + i
+        // Every token of the step attended and visible to every column of the wave.
+        const bool full = ok0 && ok1 && j * kBlockTokens + 31 <= lim_lo;
+        const bool okb = v_blk ? ok1 : ok0;  // block of this lane's tokens
+        if (!full) {
+            // Value slots past the sequence end (or of a block not attended) are
+            // zeroed: their weights are 0, and 0 * NaN must not reach the sums.
+            const int keep = okb ? min(max(L - t0, 0), 8) : 0;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) vr[t] = keep_first(vr[t], keep);
+        }
+        uint4 pb[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 sa[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) a = mfma_bf16_32(kr[t][ks], qv[ct][ks], a);
+                sa[t] = a;
+            }
+            if (!full) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!okb || t0 + 4 * t + i > lim[ct]) sa[t][i] = -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(sa[0][0], sa[0][1]), fmaxf(sa[0][2], sa[0][3])),
+                                   fmaxf(fmaxf(sa[1][0], sa[1][1]), fmaxf(sa[1][2], sa[1][3])));
+            const float mx2 = column_max(mx) * c2;
+            mt[ct] = fmaxf(mt[ct], mx2);
+            const bool grow = mx2 > m[ct] + kLazyLog2;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float alpha = !grow ? 1.f : (m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - mx2));
+                if (grow) m[ct] = mx2;
+                l[ct] *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
+            }
+            float pr[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(sa[t][i], c2, -m[ct]));
+                    // A column that has seen nothing keeps m = -inf: weight 0, not NaN.
+                    pr[t][i] = (!full && m[ct] == -INFINITY) ? 0.f : e;
+                }
+            l[ct] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) +
+                     ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
+            pb[ct] = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
+                                pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct][t] = mfma_bf16_32(vr[t], pb[ct], acc[ct][t]);
+    };
+
+    // Keys of the next step are in flight during this one (two key register
+    // sets); the values of a step are requested when it starts and arrive
+    // during its logits and softmax.
+    uint4 kA[2][KS], kB[2][KS], vr[DT];
+    int j = jb;
+    if (j < je_w) {
+        int a0, a1, b0, b1;
+        ids(j, a0, a1);
+        load_k(a0, a1, kA);
+        for (;;) {
+            load_v(a0, a1, vr);
+            ids(j + 2, b0, b1);
+            load_k(b0, b1, kB);
+            step(j, kA, vr, a0 >= 0, a1 >= 0);
+            j += 2;
+            if (j >= je_w) break;
+            load_v(b0, b1, vr);
+            ids(j + 2, a0, a1);
+            load_k(a0, a1, kA);
+            step(j, kB, vr, b0 >= 0, b1 >= 0);
+            j += 2;
+            if (j >= je_w) break;
+        }
+    }
+
+    // Results: lane (n, q) holds d = 16t + 4q + r of column cw + 16 ct + n.
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const float lc = column_sum(l[ct]);
+        const int c = cw + 16 * ct + n;
+        if (c >= ncols) continue;
+        const float inv = lc > 0.f ? 1.f / lc : 0.f;
+        if (kFinal) {
+            uint16_t *orow = out + qrow_of(c) * D + 4 * q;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const f32x4 o = acc[ct][t] * inv;
+                *reinterpret_cast<u32x2 *>(orow + 16 * t) = u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+            }
+        } else {
+            const size_t row = qrow_of(c) * max_parts + p;
+            float *orow = tmp_out + row * D + 4 * q;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4 *>(orow + 16 * t) = acc[ct][t] * inv;
+            if (q == 0) {
+                // exp-sum against the true max: sum 2^(z' - m) * 2^(m - mt).
+                exp_sums[row] = mt[ct] == -INFINITY ? 0.f : lc * __builtin_amdgcn_exp2f(m[ct] - mt[ct]);
+                max_logits[row] = mt[ct] * kLn2;
+            }
+        }
+    }
+}
+
+template <int D, int NCT, bool kFinal>
+hipError_t launch_prefill_t(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
+    const int group = pb.num_q_heads / pb.num_kv_heads;
+    const int ygroups = prefill_column_groups(group, pb.qlen, NCT);
+    dim3 grid(kFinal ? 1 : parts->max_parts, pb.num_kv_heads * ygroups, pb.num_seqs);
+    prefill_kernel<D, NCT, kFinal><<<grid, kPrefillWaves * 64, 0, stream>>>(
+        static_cast<const uint16_t *>(pb.query), static_cast<const uint16_t *>(pb.key_cache),
+        static_cast<const uint16_t *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
+        pb.num_kv_heads, group, pb.qlen, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
+        kFinal ? kBlockTokens : parts->partition_size, kFinal ? 0 : parts->max_parts,
+        kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
+        kFinal ? nullptr : parts->max_logits, static_cast<uint16_t *>(out));
+    return hipGetLastError();
+}
+
+template <int D, bool kFinal>
+hipError_t launch_prefill_d(const Problem &pb, const Partials *parts, void *out, int nct,
+                            hipStream_t stream) {
+    switch (nct) {
+        case 1: return launch_prefill_t<D, 1, kFinal>(pb, parts, out, stream);
+        case 2: return launch_prefill_t<D, 2, kFinal>(pb, parts, out, stream);
+        default: return launch_prefill_t<D, 4, kFinal>(pb, parts, out, stream);
+    }
+}
+
+}  // namespace
+
+int prefill_column_groups(int group, int qlen, int nct) {
+    const int per = kPrefillWaves * 16 * nct;
+    return (int)(((long long)group * qlen + per - 1) / per);
+}
+
+hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, int nct,
+                          hipStream_t stream) {
+    if (pb.dtype != Dtype::BF16) return hipErrorInvalidValue;
+    if (parts == nullptr) {
+        return pb.head_dim == 64 ? launch_prefill_d<64, true>(pb, nullptr, out, nct, stream)
+                                 : launch_prefill_d<128, true>(pb, nullptr, out, nct, stream);
+    }
+    return pb.head_dim == 64 ? launch_prefill_d<64, false>(pb, parts, nullptr, nct, stream)
+                             : launch_prefill_d<128, false>(pb, parts, nullptr, nct, stream);
+}
+
+}  // namespace pa

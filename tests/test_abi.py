@@ -175,3 +175,20 @@ def test_multi_query_grid_limit():
     assert lib.pa_decode_v1_q(*args) == UNSUP
     assert lib.pa_decode_v1_q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 64, 8, 128, 16, 100, 16384,
                               262144, 0.088, 1, None) == SHAPE  # q_len 0
+
+
+def test_prefill_argument_checks():
+    lib = pa.load_library()
+    # (out, query, key_cache, value_cache, block_tables, seq_lens, S, q_len, Hq, Hkv, D,
+    #  block_size, num_blocks, max_blocks, max_seq_len, scale, dtype)
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 8, 2, 128, 16, 100, 64, 1024, 0.088)
+    f32, bf16 = 0, 1
+    assert lib.pa_prefill_v1(*base, f32, 2, None) == UNSUP      # bf16 only
+    assert lib.pa_prefill_v1(*base, bf16, 3, None) == ARG       # column tiles 1, 2 or 4 (0: choose)
+    assert lib.pa_prefill_v1(*base, bf16, -1, None) == ARG
+    assert lib.pa_prefill_v2(*base, f32, 1024, FAKE, 1 << 30, 4, None) == UNSUP
+    assert lib.pa_prefill_v2(*base, bf16, 1024, FAKE, 1 << 30, 8, None) == ARG
+    assert lib.pa_prefill_v2(*base, bf16, 1024, FAKE, 16, 2, None) == WS
+    # The shape checks of the _q entry points apply unchanged.
+    assert lib.pa_prefill_v1(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 8, 2, 128, 16, 100, 64, 1024,
+                             0.088, bf16, 2, None) == SHAPE

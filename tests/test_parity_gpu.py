@@ -395,32 +395,159 @@ def test_multi_query_q1_is_plain_decode():
     assert torch.equal(o2[:, 0].view(torch.int16), db.run_v2(512).view(torch.int16))
 
 
-CHUNKED = [  # name, Hq, Hkv, q_len, lens, P: more than 16 (token, head) columns per kv head
-    ("g8_q3", 16, 2, 3, [1, 2, 40, 1000, 0], 256),
-    ("g4_q9", 8, 2, 9, [5, 9, 10, 700, 2000], 512),
-    ("prefill_q64", 8, 2, 64, [64, 100, 300, 0, 17], 128),
+CHUNKED = [  # name, dtype, D, Hq, Hkv, q_len, lens, P: more than 16 (token, head) columns per kv head
+    ("g8_q3", "bf16", 128, 16, 2, 3, [1, 2, 40, 1000, 0], 256),
+    ("g4_q9", "bf16", 128, 8, 2, 9, [5, 9, 10, 700, 2000], 512),
+    # 4 or more chunks: each wave of a workgroup owns a chunk (wave columns).
+    ("prefill_q64", "bf16", 128, 8, 2, 64, [64, 100, 300, 0, 17], 128),
+    ("wc_g8_q8", "bf16", 128, 32, 4, 8, [8, 9, 1000, 4097], 1024),
+    # 68 columns = 5 chunks: the second workgroup of a kv head has one wave with columns.
+    ("wc_g4_q17_f32", "f32", 64, 8, 2, 17, [1, 17, 18, 500, 0], 256),
+    ("wc_g1_q100_d64", "bf16", 64, 3, 3, 100, [100, 250, 33], 64),
 ]
 
 
-@pytest.mark.parametrize("name,Hq,Hkv,q_len,lens,P", CHUNKED, ids=[c[0] for c in CHUNKED])
-def test_multi_query_column_chunks(name, Hq, Hkv, q_len, lens, P):
-    """G * q_len > 16: workgroups take 16 columns each (2, 3 and 16 chunks here)."""
-    spec = wl.custom(name, 123, "bf16", Hq, Hkv, 128, lens)
+@pytest.mark.parametrize("name,dtype,D,Hq,Hkv,q_len,lens,P", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_multi_query_column_chunks(name, dtype, D, Hq, Hkv, q_len, lens, P):
+    """G * q_len > 16: 16 columns per chunk; one chunk per workgroup below 4 chunks,
+    one per wave from 4 on."""
+    spec = wl.custom(name, 123, dtype, Hq, Hkv, D, lens)
     b = wl.generate(spec)
     db = DeviceBatch(b)
     q = _multi_query(spec, q_len)
     print(f"[case] column chunks {name}", flush=True)
     _, kc, vc, bt, sl = b.numpy()
-    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype="bf16")
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype=dtype)
     out1 = torch.full_like(q, float("nan"))
     pa.pa_decode_v1_q(out1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
                       spec.scale, db.max_seq_len)
-    assert_close(to_f64(out1), ref, "bf16", f"v1 {name}")
-    ws = pa.new_workspace(spec.num_seqs, q_len * Hq, 128, db.max_seq_len, P)
+    assert_close(to_f64(out1), ref, dtype, f"v1 {name}")
+    ws = pa.new_workspace(spec.num_seqs, q_len * Hq, D, db.max_seq_len, P)
+    ws.view(torch.uint8).fill_(0xFF)
+    pa.pa_workspace_init(ws)
     out2 = torch.full_like(q, float("nan"))
     pa.pa_decode_v2_q(out2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
                       spec.scale, db.max_seq_len, P, ws)
-    assert_close(to_f64(out2), ref, "bf16", f"v2 {name}")
+    assert_close(to_f64(out2), ref, dtype, f"v2 {name}")
+
+
+# ---------------------------------------------------------------------------
+# Tiled prefill (pa_prefill_v1 / pa_prefill_v2): the q_len computation on the
+# kernel that holds several 16-column tiles per wave.
+# ---------------------------------------------------------------------------
+PREFILL = [  # name, D, Hq, Hkv, q_len, lens, P
+    ("g4_q64", 128, 8, 2, 64, [64, 100, 300, 0, 17], 128),          # 256 columns per kv head
+    ("g8_q40_d64", 64, 32, 4, 40, [40, 1000, 39, 2049], 256),       # 320: ragged wave groups
+    ("g1_q100", 128, 3, 3, 100, [100, 250, 33], 64),                # G = 1
+    ("g5_q33_p16", 128, 10, 2, 33, [33, 500, 5, 47], 16),           # G = 5; steps span partitions
+    ("g2_q7", 64, 4, 2, 7, [7, 3, 90], 32),                         # 14 columns: one partial tile
+]
+
+
+def _prefill_run(db, q, P, tiles, scale=None):
+    scale = db.spec.scale if scale is None else scale
+    out1 = torch.full_like(q, float("nan"))
+    pa.pa_prefill_v1(out1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens, scale,
+                     db.max_seq_len, tiles)
+    S, q_len, Hq, D = q.shape
+    ws = pa.new_workspace(S, q_len * Hq, D, db.max_seq_len, P)
+    ws.view(torch.uint8).fill_(0xFF)
+    pa.pa_workspace_init(ws)
+    out2 = torch.full_like(q, float("nan"))
+    pa.pa_prefill_v2(out2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens, scale,
+                     db.max_seq_len, P, ws, tiles)
+    return out1, out2
+
+
+@pytest.mark.parametrize("tiles", [1, 2, 4])
+@pytest.mark.parametrize("name,D,Hq,Hkv,q_len,lens,P", PREFILL, ids=[c[0] for c in PREFILL])
+def test_prefill(name, D, Hq, Hkv, q_len, lens, P, tiles):
+    spec = wl.custom("prefill_" + name, 125, "bf16", Hq, Hkv, D, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q = _multi_query(spec, q_len)
+    print(f"[case] prefill {name} tiles={tiles}", flush=True)
+    _, kc, vc, bt, sl = b.numpy()
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype="bf16")
+    out1, out2 = _prefill_run(db, q, P, tiles)
+    assert_close(to_f64(out1), ref, "bf16", f"prefill v1 {name} tiles={tiles}")
+    assert_close(to_f64(out2), ref, "bf16", f"prefill v2 {name} P={P} tiles={tiles}")
+
+
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.3])
+def test_prefill_scale_values(scale):
+    """Negative and zero scales: the kernel takes its maxima before scaling."""
+    spec = wl.custom("prefill_scale", 126, "bf16", 8, 2, 128, [70, 300])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q = _multi_query(spec, 24)
+    _, kc, vc, bt, sl = b.numpy()
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, scale, dtype="bf16")
+    for tiles in (1, 4):
+        out1, out2 = _prefill_run(db, q, 64, tiles, scale=scale)
+        assert_close(to_f64(out1), ref, "bf16", f"prefill v1 scale={scale}")
+        assert_close(to_f64(out2), ref, "bf16", f"prefill v2 scale={scale}")
+
+
+def test_prefill_skipped_block_ids():
+    """Ids outside [0, num_blocks) are never read and their tokens leave every
+    query's softmax; positions (and so the causal limits) do not move.  Reference:
+    the oracle's single-query decode of each query token over its visible tokens
+    with the skipped blocks' tokens removed."""
+    spec = wl.custom("prefill_badids", 127, "bf16", 8, 2, 64, [100, 70])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    bt = b.block_tables.clone()
+    bt[0, 2] = -7
+    bt[1, 0] = b.key_cache.shape[0] + 3
+    db.block_tables = bt.to("cuda")
+    q_len = 40
+    q = _multi_query(spec, q_len)
+    qn = wl.to_numpy(q.cpu())
+    _, kc, vc, bt_np, _ = b.numpy_logical()
+    skip = {0: {2}, 1: {0}}
+    ref = np.zeros(q.shape, np.float64)
+    for s, L in ((0, 100), (1, 70)):
+        for j in range(q_len):
+            toks = [t for t in range(L - q_len + j + 1) if (t // 16) not in skip[s]]
+            n = len(toks)
+            if n == 0:
+                continue
+            nb = -(-n // 16)
+            kk = np.full((nb, 2, 16, 64), 0x7FC0, np.uint16)  # bf16 NaN bit patterns
+            vv = np.full((nb, 2, 16, 64), 0x7FC0, np.uint16)
+            for i, t in enumerate(toks):
+                kk[i // 16, :, i % 16] = kc[bt_np[s, t // 16], :, t % 16]
+                vv[i // 16, :, i % 16] = vc[bt_np[s, t // 16], :, t % 16]
+            ref[s, j] = oracle.decode(np.ascontiguousarray(qn[s, j][None]), *wl.pack_kv(kk, vv, 2),
+                                      np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
+                                      spec.scale, dtype="bf16")[0]
+    for tiles in (2, 4):
+        out1, out2 = _prefill_run(db, q, 32, tiles)
+        assert_close(to_f64(out1), ref, "bf16", "prefill v1 skipped ids")
+        assert_close(to_f64(out2), ref, "bf16", "prefill v2 skipped ids")
+
+
+def test_prefill_long_sampled():
+    """q_len 512 over an 8192-token cache (Hq 32, Hkv 4, D 128) in the launch shapes
+    the prefill timings use; sampled query tokens against the oracle's single-query
+    decode over each token's visible prefix (L - q_len + j + 1 tokens)."""
+    spec = wl.custom("prefill_long", 128, "bf16", 32, 4, 128, [8192])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q_len = 512
+    q = _multi_query(spec, q_len)
+    qn = wl.to_numpy(q.cpu())
+    _, kc, vc, bt, _ = b.numpy()
+    js = np.array([0, 1, 15, 16, 200, 383, 510, 511])
+    ref = oracle.decode(np.ascontiguousarray(qn[0, js]), kc, vc, np.repeat(bt, len(js), 0),
+                        (8192 - q_len + js + 1).astype(np.int32), spec.scale, dtype="bf16")
+    for tiles in (2, 4):
+        out1, out2 = _prefill_run(db, q, 1024, tiles)
+        for out, what in ((out1, "v1"), (out2, "v2")):
+            got = to_f64(out)
+            assert np.all(np.isfinite(got)), what
+            assert_close(got[0, js], ref, "bf16", f"prefill long {what} tiles={tiles}")
 
 
 def test_graph_capture_replays():
