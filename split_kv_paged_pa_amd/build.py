@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libpa_decode.so")
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # (source, flags of its own)
 SOURCES = [(os.path.join(CSRC, "pa_kernels.hip"), VGPR_FORM),
-           (os.path.join(CSRC, "pa_prefill.hip"), []),
+           (os.path.join(CSRC, "pa_prefill.hip"), VGPR_FORM),
            (os.path.join(CSRC, "pa_api.cpp"), [])]
 PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
 PROBE_SOURCES = [(os.path.join(CSRC, "pa_probe.hip"), VGPR_FORM)]

@@ -49,6 +49,9 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Staging registers: a native vector (plain loads and stores; HIP's uint4 is a
+// struct whose copies through an array stay in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPrefillWaves = 4;
 // A column's reference max moves when a logit exceeds it by more than this (log2 units).
@@ -88,16 +91,29 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     constexpr int DT = D / 16;       // 16-row d tiles of the output
     constexpr int WCOLS = 16 * NCT;  // columns per wave
     constexpr int NW = kPrefillWaves;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int kSlab = kBlockTokens * D * 2;  // bytes of one (block, kv head) slab
+    constexpr int kPieces = kSlab / 16;          // 16-byte pieces per slab
+    constexpr int kLoads = 4 * kPieces / (NW * 64);  // pieces per thread per step
+    // LDS ring: kStages stages of four regions (keys of the step's two blocks,
+    // then their values).  Regions are kSlab + 128 bytes apart: the two key
+    // regions start half a 256-byte bank line apart (see the reads below).
+    constexpr int kRegion = kSlab + 128;
+    constexpr int kStage = 4 * kRegion;
+    constexpr int kStages = 3;
+    __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15;  // column of a tile; row of the A operands
     const int q = lane >> 4;  // lane group: k slots 8q .. 8q+7, result rows 4q .. 4q+3
 
     const int ncols = group * qlen;
     const int ygroups = (ncols + NW * WCOLS - 1) / (NW * WCOLS);
     const int kvh = blockIdx.y / ygroups;
-    const int cw = ((blockIdx.y - kvh * ygroups) * NW + w) * WCOLS;  // first column of the wave
-    if (cw >= ncols) return;  // no barrier in this kernel: a wave without columns just leaves
+    const int cg = (blockIdx.y - kvh * ygroups) * NW * WCOLS;  // first column of the workgroup
+    const int cw = cg + w * WCOLS;                              // first column of this wave
+    const bool has_cols = cw < ncols;  // a wave without columns still loads and waits
     const int s = blockIdx.z;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
@@ -105,7 +121,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     if (!kFinal) {
         const int bp = partition_size / kBlockTokens;
         p = blockIdx.x;
-        if (p >= (nblk + bp - 1) / bp) return;  // past the sequence: never read
+        if (p >= (nblk + bp - 1) / bp) return;  // uniform: past the sequence, never read
         jb = p * bp;
         je = min(jb + bp, nblk);
     }
@@ -128,20 +144,27 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     for (int ct = 0; ct < NCT; ++ct) {
         const int c = cw + 16 * ct + n;
         lim[ct] = c < ncols ? L - qlen + c / group : L - 1;
-        const uint4 *src = reinterpret_cast<const uint4 *>(query + qrow_of(c) * D) + q;
+        const uint4 *src = reinterpret_cast<const uint4 *>(query + qrow_of(min(c, ncols - 1)) * D) + q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uint4 v = c < ncols ? src[4 * ks] : make_uint4(0, 0, 0, 0);
             qv[ct][ks] = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
         }
     }
-    const int c_last = min(cw + WCOLS, ncols) - 1;
-    const int lim_lo = L - qlen + cw / group;      // smallest limit of the wave's columns
-    const int lim_hi = L - qlen + c_last / group;  // largest
-    // Blocks past lim_hi are invisible to every column of the wave.
-    const int je_w = lim_hi < 0 ? jb : max(jb, min(je, lim_hi / kBlockTokens + 1));
+    // Causal range: the wave computes up to its own last column's limit, the
+    // workgroup loads up to the last limit of all its columns.  These are uniform
+    // (over the wave, the workgroup); readfirstlane keeps them in scalar
+    // registers, so the loop control and the block ids stay scalar.
+    const int lim_lo = __builtin_amdgcn_readfirstlane(L - qlen + cw / group);  // smallest of the wave
+    const int lim_hi = __builtin_amdgcn_readfirstlane(
+        has_cols ? L - qlen + (min(cw + WCOLS, ncols) - 1) / group : -1);
+    const int lim_wg = L - qlen + (min(cg + NW * WCOLS, ncols) - 1) / group;
+    const int je_g = __builtin_amdgcn_readfirstlane(
+        lim_wg < 0 ? jb : max(jb, min(je, lim_wg / kBlockTokens + 1)));
+    // Steps of two blocks; none without any cache block (every id would be skipped).
+    const int nsteps = num_blocks > 0 ? (je_g - jb + 1) / 2 : 0;
 
-    float m[NCT], mt[NCT], l[NCT];    // reference max, true max (log2 units), lane's exp-sum share
+    float m[NCT], mt[NCT], l[NCT];  // reference max, true max (log2 units), lane's exp-sum share
     f32x4 acc[NCT][DT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -152,135 +175,206 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         for (int t = 0; t < DT; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Byte offsets in a (block, kv head) slab.  Keys [D/8][16][8]: A row n of tile
-    // T is token 8*((n/4)%2) + 4T + n%4 of block n/8 (of the step's two), d chunk
-    // 4 ks + q.  Values [D][16]: lane (n, q) reads row d = 16t + n, tokens
-    // 8*(q%2) .. +7 of block q/2.
-    constexpr int kSlabBytes = kBlockTokens * D * 2;
-    const int k_blk = n >> 3;
-    const int k_off = q * 256 + (8 * ((n >> 2) & 1) + (n & 3)) * 16;
-    const int v_blk = q >> 1;
-    const int v_off = n * 32 + (q & 1) * 16;
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
-    const char *kbase = reinterpret_cast<const char *>(key_cache) + (size_t)kvh * kSlabBytes;
-    const char *vbase = reinterpret_cast<const char *>(value_cache) + (size_t)kvh * kSlabBytes;
-    const size_t blk_stride = (size_t)num_kv_heads * kSlabBytes;
-    // Loads of a block that is not attended read the first 16 bytes of the
-    // wave's first query row instead, so every step issues the same loads.
-    const char *dummy = reinterpret_cast<const char *>(query + qrow_of(cw) * D);
+    const char *kbase = reinterpret_cast<const char *>(key_cache) + (size_t)kvh * kSlab;
+    const char *vbase = reinterpret_cast<const char *>(value_cache) + (size_t)kvh * kSlab;
+    const size_t blk_stride = (size_t)num_kv_heads * kSlab;
 
     // Block ids of the step at block j (blocks j, j + 1); -1: not attended.
     auto ids = [&](int j, int &id0, int &id1) {
-        id0 = j < je_w ? bt[j] : -1;
-        id1 = j + 1 < je_w ? bt[j + 1] : -1;
+        id0 = j < je_g ? bt[j] : -1;
+        id1 = j + 1 < je_g ? bt[j + 1] : -1;
         if ((unsigned)id0 >= (unsigned)num_blocks) id0 = -1;
         if ((unsigned)id1 >= (unsigned)num_blocks) id1 = -1;
     };
-    auto load_k = [&](int id0, int id1, uint4 (&kr)[2][KS]) {
-        const bool kok = (k_blk ? id1 : id0) >= 0;
-        const char *kp = kok ? kbase + (size_t)(k_blk ? id1 : id0) * blk_stride + k_off : dummy;
-        const int kstep = kok ? 1024 : 0, ktile = kok ? 64 : 0;
+    // Piece k = tid + 256 i of a step: region r = k / kPieces (keys of block 0,
+    // keys of block 1, values of block 0, values of block 1), piece k % kPieces.
+    // With D = 128 load i is region i; with D = 64 it is region 2i + tid / 128.
+    // A block that is not attended is replaced by block 0 of the same kv head
+    // (valid memory; its tokens are masked), so every step issues the same loads.
+    auto fetch = [&](int id0, int id1, u32x4 (&st)[kLoads]) {
+        const size_t o0 = (size_t)max(id0, 0) * blk_stride, o1 = (size_t)max(id1, 0) * blk_stride;
+        const char *base[4] = {kbase + o0, kbase + o1, vbase + o0, vbase + o1};  // uniform
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const char *src;
+            if constexpr (kLoads == 4) {
+                src = base[i] + tid * 16;
+            } else {
+                const int hi = tid >= kPieces;
+                src = (hi ? base[2 * i + 1] : base[2 * i]) + (tid - hi * kPieces) * 16;
+            }
+            st[i] = *reinterpret_cast<const u32x4 *>(src);
+        }
+    };
+    // Values are stored with piece x (row x / 2, token half x % 2) at position
+    // x ^ ((x >> 4) & 1): the 16 lanes that read one half of rows 16t .. 16t+15
+    // then hit 16 different 16-byte bank groups.
+    // LDS positions (16-byte units) inside a region, chosen so that every group
+    // of 8 (and of 16) lanes of an operand read touches distinct banks:
+    //   keys, piece (chunk c, token t) -> 16c + (t ^ 4 * (t / 8));
+    //   values, piece x (row x / 2, token half x % 2) -> x ^ ((x / 8 ^ x / 16) & 1).
+    int st_off[kLoads];  // LDS byte offset of this thread's piece i inside a stage
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int k = tid + NW * 64 * i;
+        const int r = k / kPieces;
+        const int pc = k - r * kPieces;
+        const int pos = r < 2 ? (pc ^ (((pc >> 3) & 1) << 2)) : (pc ^ (((pc >> 3) ^ (pc >> 4)) & 1));
+        st_off[i] = r * kRegion + pos * 16;
+    }
+    auto stash = [&](int stage, const u32x4 (&st)[kLoads]) {
+        char *dst = lds + stage * kStage;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4 *>(dst + st_off[i]) = st[i];
+    };
+
+    // LDS offsets of the operands.  Keys [D/8][16][8]: A row n of tile T is token
+    // t = 8b + 4T + n%4 (b = (n/4)%2) of block n/8, d chunk 4 ks + q, stored at
+    // token slot t ^ 4b = 8b + 4(T ^ b) + n%4.  Values [D][16]: lane (n, q) reads
+    // row d = 16t + n, tokens 8*(q%2) .. +7 of block q/2.
+    const int kb_ = (n >> 2) & 1;
+    const int k_lds0 = (n >> 3) * kRegion + q * 256 + (8 * kb_ + 4 * kb_ + (n & 3)) * 16;        // T = 0
+    const int k_lds1 = (n >> 3) * kRegion + q * 256 + (8 * kb_ + 4 * (1 - kb_) + (n & 3)) * 16;  // T = 1
+    // Value piece x = 32t + 2n + q%2 of d tile t: its swizzle bit depends on bits
+    // 3 and 4 of x only, i.e. on n, so position = 32t + const: one lane offset
+    // plus 512t.
+    const int vx = 2 * n + (q & 1);
+    const int v_lds = (2 + (q >> 1)) * kRegion + (vx ^ (((vx >> 3) ^ (vx >> 4)) & 1)) * 16;
+
+    // One step of 32 tokens from LDS stage `stage`: logits, reference update,
+    // weights, PV.
+    auto step = [&](int j, int stage, bool ok0, bool ok1) {
+        const char *sk0 = lds + stage * kStage + k_lds0;
+        const char *sk1 = lds + stage * kStage + k_lds1;
+        const char *sv = lds + stage * kStage + v_lds;  // + 512 t for d tile t
+        const int t0 = j * kBlockTokens + 8 * q;  // lane's first token: t0 + 4T + i
+        // Every token of the step attended and visible to every column of the wave.
+        const bool full = ok0 && ok1 && j * kBlockTokens + 31 <= lim_lo;
+        const bool okb = (q >> 1) ? ok1 : ok0;  // block of this lane's tokens
+        uint4 kr[2][KS];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kr[t][ks] = *reinterpret_cast<const uint4 *>(kp + ks * kstep + t * ktile);
-    };
-    auto load_v = [&](int id0, int id1, uint4 (&vr)[DT]) {
-        const bool vok = (v_blk ? id1 : id0) >= 0;
-        const char *vp = vok ? vbase + (size_t)(v_blk ? id1 : id0) * blk_stride + v_off : dummy;
-        const int vstep = vok ? 512 : 0;
+                kr[t][ks] = *reinterpret_cast<const uint4 *>((t ? sk1 : sk0) + ks * 1024);
+        // Logits of every tile first, so that the MFMAs run back to back.
+        f32x4 sa[NCT][2];
 #pragma unroll
-        for (int t = 0; t < DT; ++t) vr[t] = *reinterpret_cast<const uint4 *>(vp + t * vstep);
-    };
-
-    // One step of 32 tokens: logits, reference update, weights, PV.
-    auto step = [&](int j, const uint4 (&kr)[2][KS], uint4 (&vr)[DT], bool ok0, bool ok1) {
-        const int t0 = j * kBlockTokens + 8 * q;  // lane's first token: t0 + 4T + i
-        // Every token of the step attended and visible to every column of the wave.
-        const bool full = ok0 && ok1 && j * kBlockTokens + 31 <= lim_lo;
-        const bool okb = v_blk ? ok1 : ok0;  // block of this lane's tokens
-        if (!full) {
-            // Value slots past the sequence end (or of a block not attended) are
-            // zeroed: their weights are 0, and 0 * NaN must not reach the sums.
-            const int keep = okb ? min(max(L - t0, 0), 8) : 0;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) vr[t] = keep_first(vr[t], keep);
-        }
-        uint4 pb[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 sa[2];
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) a = mfma_bf16_32(kr[t][ks], qv[ct][ks], a);
-                sa[t] = a;
+                sa[ct][t] = a;
             }
-            if (!full) {
+        if (!full) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!okb || t0 + 4 * t + i > lim[ct]) sa[t][i] = -INFINITY;
-            }
-            const float mx = fmaxf(fmaxf(fmaxf(sa[0][0], sa[0][1]), fmaxf(sa[0][2], sa[0][3])),
-                                   fmaxf(fmaxf(sa[1][0], sa[1][1]), fmaxf(sa[1][2], sa[1][3])));
-            const float mx2 = column_max(mx) * c2;
-            mt[ct] = fmaxf(mt[ct], mx2);
-            const bool grow = mx2 > m[ct] + kLazyLog2;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float alpha = !grow ? 1.f : (m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - mx2));
-                if (grow) m[ct] = mx2;
+                        if (!okb || t0 + 4 * t + i > lim[ct]) sa[ct][t][i] = -INFINITY;
+        }
+        // Column maxima; one wave-uniform branch covers the (rare) moves of the
+        // reference max of any tile.
+        float mx2[NCT];
+        bool grow_any = false;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 a = sa[ct][0], b = sa[ct][1];
+            const float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                                   fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+            mx2[ct] = column_max(mx) * c2;
+            mt[ct] = fmaxf(mt[ct], mx2[ct]);
+            grow_any |= mx2[ct] > m[ct] + kLazyLog2;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const bool grow = mx2[ct] > m[ct] + kLazyLog2;
+                const float alpha = !grow ? 1.f : (m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - mx2[ct]));
+                if (grow) m[ct] = mx2[ct];
                 l[ct] *= alpha;
 #pragma unroll
                 for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
             }
+        }
+        uint4 pb[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
             float pr[2][4];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(sa[t][i], c2, -m[ct]));
-                    // A column that has seen nothing keeps m = -inf: weight 0, not NaN.
-                    pr[t][i] = (!full && m[ct] == -INFINITY) ? 0.f : e;
-                }
+                for (int i = 0; i < 4; ++i) pr[t][i] = __builtin_amdgcn_exp2f(fmaf(sa[ct][t][i], c2, -m[ct]));
+            if (!full) {
+                // A column that has seen nothing keeps m = -inf: weights 0, not NaN.
+                const bool dead = m[ct] == -INFINITY;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pr[t][i] = dead ? 0.f : pr[t][i];
+            }
             l[ct] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) +
                      ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
             pb[ct] = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
                                 pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
         }
+        uint4 vv[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vv[t] = *reinterpret_cast<const uint4 *>(sv + 512 * t);
+        if (!full) {
+            // Value slots past the sequence end (or of a block not attended) are
+            // zeroed: their weights are 0, and 0 * NaN must not reach the sums.
+            const int keep = okb ? min(max(L - t0, 0), 8) : 0;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) vv[t] = keep_first(vv[t], keep);
+        }
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[ct][t] = mfma_bf16_32(vr[t], pb[ct], acc[ct][t]);
+            for (int ct = 0; ct < NCT; ++ct) acc[ct][t] = mfma_bf16_32(vv[t], pb[ct], acc[ct][t]);
     };
 
-    // Keys of the next step are in flight during this one (two key register
-    // sets); the values of a step are requested when it starts and arrive
-    // during its logits and softmax.
-    uint4 kA[2][KS], kB[2][KS], vr[DT];
-    int j = jb;
-    if (j < je_w) {
-        int a0, a1, b0, b1;
-        ids(j, a0, a1);
-        load_k(a0, a1, kA);
-        for (;;) {
-            load_v(a0, a1, vr);
-            ids(j + 2, b0, b1);
-            load_k(b0, b1, kB);
-            step(j, kA, vr, a0 >= 0, a1 >= 0);
-            j += 2;
-            if (j >= je_w) break;
-            load_v(b0, b1, vr);
-            ids(j + 2, a0, a1);
-            load_k(a0, a1, kA);
-            step(j, kB, vr, b0 >= 0, b1 >= 0);
-            j += 2;
-            if (j >= je_w) break;
+    // Pipeline: the loads of step i + 2 are issued when step i starts, held in
+    // registers, and written to the LDS ring after step i + 1 has computed, so
+    // global latency has two steps to hide; one barrier per step.  Stage
+    // (i + 1) % 3, written at the end of step i, was last read in step i - 2,
+    // which every wave finished before the barrier of step i - 1.
+    if (nsteps > 0) {
+        u32x4 stA[kLoads], stB[kLoads];
+        int a0, a1, b0, b1, c0, c1;  // block ids of steps i, i + 1, i + 2
+        ids(jb, a0, a1);
+        fetch(a0, a1, stA);
+        stash(0, stA);
+        ids(jb + 2, b0, b1);
+        fetch(b0, b1, stB);  // past the end the loads read block 0 (never used)
+        for (int i = 0; i < nsteps; i += 2) {
+            // step i: stage i % 3; stB holds step i + 1
+            __syncthreads();
+            ids(jb + 2 * (i + 2), c0, c1);
+            fetch(c0, c1, stA);
+            if (has_cols && (jb + 2 * i) * kBlockTokens <= lim_hi) step(jb + 2 * i, i % 3, a0 >= 0, a1 >= 0);
+            if (i + 1 < nsteps) {  // uniform over the workgroup
+                stash((i + 1) % 3, stB);
+                a0 = c0;
+                a1 = c1;
+                // step i + 1: stage (i + 1) % 3; stA holds step i + 2
+                __syncthreads();
+                ids(jb + 2 * (i + 3), c0, c1);
+                fetch(c0, c1, stB);
+                if (has_cols && (jb + 2 * (i + 1)) * kBlockTokens <= lim_hi)
+                    step(jb + 2 * (i + 1), (i + 1) % 3, b0 >= 0, b1 >= 0);
+                stash((i + 2) % 3, stA);  // past the end: never read
+                b0 = c0;
+                b1 = c1;
+            }
         }
     }
+    if (!has_cols) return;
 
     // Results: lane (n, q) holds d = 16t + 4q + r of column cw + 16 ct + n.
 #pragma unroll
