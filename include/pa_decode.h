@@ -199,11 +199,13 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
  * (causal over the cache); a token that sees no token (L < q_len - j) gets a
  * zero row.  This extends the decode step along the q_len dimension that the
  * pages batch next to the GQA group (commit 490ff98, the summary_statistics
- * message).  Each (token, head) pair is one column of the kernel's 16-wide
- * tiles; a workgroup takes 16 columns of a kv head, so up to
+ * message).  Each (token, head) pair is one column of the kernels' 16-wide
+ * tiles.  The decode kernel gives a workgroup 16 columns of a kv head, so up to
  * (num_q_heads / num_kv_heads) * q_len = 16 the keys and values are read once,
- * and beyond that once per 16 columns (a plain paged prefill, correct for any
- * q_len but not tiled for reuse).  num_kv_heads * ceil(G * q_len / 16) must not
+ * and beyond that once per 16 columns; for many columns (bf16) these entry
+ * points switch to the tiled prefill kernel of pa_prefill_v1 / pa_prefill_v2,
+ * as pa_select_q_kernel reports (results then agree to rounding, not bit for
+ * bit, with the decode kernel's).  num_kv_heads * ceil(G * q_len / 16) must not
  * exceed 65535, else PA_ERR_UNSUPPORTED.
  * pa_decode_v1_q is the single pass.  pa_decode_v2_q is split-KV in two
  * launches; its workspace holds q_len * num_q_heads rows per sequence, i.e.
@@ -260,6 +262,22 @@ pa_status_t pa_prefill_v2(void *out, const void *query, const void *key_cache,
                           int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
                           int partition_size, void *workspace, size_t workspace_bytes,
                           int column_tiles, void *stream);
+
+/*
+ * Kernel that pa_decode_v1_q (single_pass = 1) or pa_decode_v2_q (single_pass
+ * = 0, partitions of partition_size tokens) runs for this shape: 0 = the decode
+ * kernel (16 (query token, head) columns per workgroup, the blocks of a
+ * partition split over its waves); 1 or 2 = the tiled prefill kernel of
+ * pa_prefill_v1 / pa_prefill_v2 with that many 16-column tiles per wave.  The
+ * prefill kernel is chosen for bf16 when a kv head has at least 64 (single
+ * pass) or 128 (split) columns G * q_len and the grid keeps enough waves for
+ * the device's compute units (two tiles at two or more waves per SIMD; one
+ * tile otherwise, or -- single pass -- the decode kernel below one wave per
+ * SIMD).  Invalid arguments give 0.  Host-only; 256 compute units are assumed
+ * when no device is visible.
+ */
+int pa_select_q_kernel(int single_pass, int num_seqs, int q_len, int num_q_heads, int num_kv_heads,
+                       pa_dtype_t dtype, int max_seq_len, int partition_size);
 
 /* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
  * for partitions p < ceil(L / partition_size) of each sequence; other entries

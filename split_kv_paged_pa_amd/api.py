@@ -9,7 +9,7 @@ Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
 pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_select_v2_auto,
 pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_prefill_v1,
-pa_prefill_v2, pa_status_string.
+pa_prefill_v2, pa_select_q_kernel, pa_status_string.
 """
 from __future__ import annotations
 
@@ -68,6 +68,8 @@ def load_library():
     lib.pa_decode_v1_q.restype = I
     lib.pa_decode_v2_q.argtypes = [P] + common_q + [I, P, Z, P]
     lib.pa_decode_v2_q.restype = I
+    lib.pa_select_q_kernel.argtypes = [I, I, I, I, I, I, I, I]
+    lib.pa_select_q_kernel.restype = I
     lib.pa_prefill_v1.argtypes = [P] + common_q + [I, P]
     lib.pa_prefill_v1.restype = I
     lib.pa_prefill_v2.argtypes = [P] + common_q + [I, P, Z, I, P]
@@ -279,6 +281,16 @@ def pa_decode_v2_q(out, query, key_cache, value_cache, block_tables, seq_lens, s
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode_v2_q(o, *args, int(partition_size), wp, wb, _stream(stream)),
            "pa_decode_v2_q")
+
+
+def pa_select_q_kernel(single_pass, num_seqs, q_len, num_q_heads, num_kv_heads, dtype,
+                       max_seq_len, partition_size=1024):
+    """Kernel the q_len entry points use: 0 = decode kernel, 1 or 2 = prefill kernel tiles.
+    dtype: torch.float32 / torch.bfloat16."""
+    return int(load_library().pa_select_q_kernel(int(bool(single_pass)), int(num_seqs), int(q_len),
+                                                 int(num_q_heads), int(num_kv_heads),
+                                                 _DTYPE_CODE[dtype], int(max_seq_len),
+                                                 int(partition_size)))
 
 
 def pa_prefill_v1(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,

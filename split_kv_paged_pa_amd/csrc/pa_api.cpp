@@ -164,15 +164,45 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// tiles: 0 = decode kernel; 1, 2 or 4 = prefill kernel (bf16 only).
+// Kernel selection of decode_v1 / decode_v2 (their tiles argument):
+//   0          the decode kernel;
+//   1, 2, 4    the prefill kernel with that many 16-column tiles per wave (bf16);
+//   kAuto      the library's choice between the two (auto_tiles);
+//   kAutoPrefill  the prefill kernel, tiles chosen by the library.
+constexpr int kAuto = -1;
+constexpr int kAutoPrefill = -2;
+
 pa_status_t check_tiles(int tiles, pa_dtype_t dtype) {
-    if (tiles == 0) return PA_OK;
-    if (tiles != 1 && tiles != 2 && tiles != 4) return PA_ERR_INVALID_ARGUMENT;
+    if (tiles == 0 || tiles == kAuto) return PA_OK;
+    if (tiles != 1 && tiles != 2 && tiles != 4 && tiles != kAutoPrefill)
+        return PA_ERR_INVALID_ARGUMENT;
     return dtype == PA_DTYPE_BF16 ? PA_OK : PA_ERR_UNSUPPORTED;
 }
 
-// Column tiles per wave when the caller leaves the choice to the library.
-int default_tiles(int head_dim) { return head_dim == 64 ? 4 : 2; }
+// Kernel for the q_len entry points (tiles argument of decode_v1 / decode_v2):
+// 0 = the decode kernel (16 columns per workgroup, blocks split over its waves),
+// 1 or 2 = the prefill kernel with that many 16-column tiles per wave.  The
+// prefill kernel reads each key/value block once per 64 * tiles columns instead
+// of once per 16, which pays once a kv head has many (query token, head)
+// columns and the grid still has enough waves: two tiles when that leaves at
+// least two waves per SIMD, one tile when it leaves one (single pass) or when
+// the partitions make up the parallelism (split-KV).  Measured on MI355X
+// (S 1, Hq 32, Hkv 4, D 128): q_len 512 / 8192 tokens 216 -> 185 us single pass,
+// 321 -> 147 us split at P 1024; q_len 8 keeps the decode kernel.
+// prefill_only: the caller asked for the prefill kernel; the answer is then
+// 1 or 2, never 0.
+int auto_tiles(bool single_pass, bool prefill_only, int num_seqs, int num_kv_heads, int group,
+               int q_len, pa_dtype_t dtype, int max_parts) {
+    if (dtype != PA_DTYPE_BF16) return 0;
+    const long long cols = (long long)group * q_len;
+    if (!prefill_only && cols < (single_pass ? 64 : 128)) return 0;
+    int cus = compute_units();
+    if (cus <= 0) cus = 256;
+    const long long units = (long long)num_seqs * num_kv_heads * (single_pass ? 1 : max(max_parts, 1));
+    if (units * ((cols + 31) / 32) >= 8LL * cus) return 2;
+    if (!single_pass || prefill_only) return 1;
+    return units * ((cols + 15) / 16) >= 4LL * cus ? 1 : 0;
+}
 
 // The single launch applies when every (sequence, kv head) has a counter slot
 // and the last workgroup's merge fits its weight table.
@@ -254,6 +284,9 @@ pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
     if (st != PA_OK) return st;
     st = check_tiles(tiles, dtype);
     if (st != PA_OK || num_seqs == 0) return st;
+    if (tiles < 0)
+        tiles = auto_tiles(true, tiles == kAutoPrefill, num_seqs, num_kv_heads,
+                           num_q_heads / num_kv_heads, q_len, dtype, 1);
     if (!out) return PA_ERR_NULL_POINTER;
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -288,6 +321,9 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
                partition_size, workspace, workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (want_out && !out) return PA_ERR_NULL_POINTER;
+    if (tiles < 0)
+        tiles = auto_tiles(false, tiles == kAutoPrefill, num_seqs, num_kv_heads,
+                           num_q_heads / num_kv_heads, q_len, dtype, parts.max_parts);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -324,7 +360,7 @@ pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
                            pa_dtype_t dtype, void *stream) {
     return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, q_len,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                     max_blocks_per_seq, max_seq_len, scale, dtype, 0, stream);
+                     max_blocks_per_seq, max_seq_len, scale, dtype, kAuto, stream);
 }
 
 pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
@@ -381,7 +417,7 @@ pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
     return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                      q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
-                     workspace_bytes, 0, stream);
+                     workspace_bytes, kAuto, stream);
 }
 
 pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_cache,
@@ -417,7 +453,8 @@ pa_status_t pa_prefill_v1(void *out, const void *query, const void *key_cache,
                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
                           int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
                           int column_tiles, void *stream) {
-    if (column_tiles == 0) column_tiles = default_tiles(head_dim);
+    if (column_tiles == 0) column_tiles = kAutoPrefill;
+    else if (column_tiles < 0) return PA_ERR_INVALID_ARGUMENT;
     return decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs, q_len,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, column_tiles, stream);
@@ -430,11 +467,26 @@ pa_status_t pa_prefill_v2(void *out, const void *query, const void *key_cache,
                           int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype_t dtype,
                           int partition_size, void *workspace, size_t workspace_bytes,
                           int column_tiles, void *stream) {
-    if (column_tiles == 0) column_tiles = default_tiles(head_dim);
+    if (column_tiles == 0) column_tiles = kAutoPrefill;
+    else if (column_tiles < 0) return PA_ERR_INVALID_ARGUMENT;
     return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                      q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
                      workspace_bytes, column_tiles, stream);
+}
+
+int pa_select_q_kernel(int single_pass, int num_seqs, int q_len, int num_q_heads, int num_kv_heads,
+                       pa_dtype_t dtype, int max_seq_len, int partition_size) {
+    if (num_seqs <= 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || max_seq_len < 0)
+        return 0;
+    int parts = 1;
+    if (!single_pass) {
+        if (partition_size < kBlockTokens || partition_size % kBlockTokens != 0) return 0;
+        parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
+    }
+    return auto_tiles(single_pass != 0, false, num_seqs, num_kv_heads, num_q_heads / num_kv_heads,
+                      q_len, dtype, parts);
 }
 
 int pa_select_v2_auto(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {

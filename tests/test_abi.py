@@ -192,3 +192,22 @@ def test_prefill_argument_checks():
     # The shape checks of the _q entry points apply unchanged.
     assert lib.pa_prefill_v1(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 8, 2, 128, 16, 100, 64, 1024,
                              0.088, bf16, 2, None) == SHAPE
+
+
+def test_q_kernel_rule():
+    """The q_len entry points' kernel choice (no device here: 256 compute units)."""
+    import torch
+    if torch.cuda.is_available():
+        return  # the rule depends on the device's compute units
+    bf, f32 = torch.bfloat16, torch.float32
+    sel = pa.pa_select_q_kernel
+    # S 1, Hq 32, Hkv 4: q_len 512 over 8192 tokens.
+    assert sel(1, 1, 512, 32, 4, bf, 8192) == 1       # 1024 single-tile waves = 1 per SIMD
+    assert sel(0, 1, 512, 32, 4, bf, 8192, 1024) == 2  # 8 partitions: 4096 two-tile waves
+    assert sel(1, 1, 2048, 32, 4, bf, 8192) == 2      # 2048 two-tile waves
+    assert sel(1, 1, 128, 32, 4, bf, 4096) == 0       # 256 waves: the decode kernel
+    assert sel(0, 1, 8, 32, 4, bf, 8192, 1024) == 0   # 64 columns: the decode kernel
+    assert sel(0, 1, 16, 32, 4, bf, 8192, 512) == 1   # 128 columns, 16 partitions
+    assert sel(1, 1, 2048, 32, 4, f32, 8192) == 0     # fp32: the decode kernel
+    assert sel(1, 1, 1, 32, 4, bf, 8192) == 0         # plain decode
+    assert sel(0, 1, 512, 32, 4, bf, 8192, 24) == 0   # invalid partition size

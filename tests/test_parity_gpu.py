@@ -548,6 +548,20 @@ def test_prefill_long_sampled():
             got = to_f64(out)
             assert np.all(np.isfinite(got)), what
             assert_close(got[0, js], ref, "bf16", f"prefill long {what} tiles={tiles}")
+    # The q_len entry points take the prefill kernel at this shape on their own.
+    assert pa.pa_select_q_kernel(1, 1, q_len, 32, 4, torch.bfloat16, 8192) > 0
+    assert pa.pa_select_q_kernel(0, 1, q_len, 32, 4, torch.bfloat16, 8192, 1024) > 0
+    o1 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v1_q(o1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len)
+    ws = pa.new_workspace(1, q_len * 32, 128, db.max_seq_len, 1024)
+    o2 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v2_q(o2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len, 1024, ws)
+    for out, what in ((o1, "v1_q"), (o2, "v2_q")):
+        got = to_f64(out)
+        assert np.all(np.isfinite(got)), what
+        assert_close(got[0, js], ref, "bf16", f"prefill long via {what}")
 
 
 def test_graph_capture_replays():
