@@ -37,6 +37,7 @@ import split_kv_paged_pa_amd as pa  # noqa: E402
 from split_kv_paged_pa_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
 METRIC = "KV GB/s read and % of HBM peak; decode-attn µs/step at 100K ctx, GQA 8"
 # Sources of the decode kernels (the Phase-1 kernel whose traffic profiles/ records).
 KERNEL_SRC = [os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", f)
@@ -67,6 +68,35 @@ def phase1_bytes(spec, P):
     tables = int(np.sum(-(-lens // 16))) * 4 + spec.num_seqs * 4
     partials = parts * spec.num_q_heads * (spec.head_dim + 2) * 4
     return kv + q + tables + partials, kv
+
+
+def prefill_extra(dev, stream, dtype, kc, vc, bt, spec, S, Hq, D, q_len=2048, L=8192):
+    """q_len query tokens per sequence over the first L tokens of the workload's
+    cache through pa_decode_v1_q (which takes the tiled prefill kernel at this
+    size): microseconds per call and MFMA throughput, 4 * D flops per visible
+    (query token, head, cache token)."""
+    qp = torch.randn(S, q_len, Hq, D, device=dev).to(dtype)
+    op = torch.empty_like(qp)
+    slp = torch.full((S,), L, dtype=torch.int32, device=dev)
+
+    def run():
+        pa.pa_decode_v1_q(op, qp, kc, vc, bt, slp, spec.scale, L)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 10
+    pairs = S * Hq * sum(L - q_len + j + 1 for j in range(q_len))
+    tflops = 4.0 * D * pairs / (us * 1e-6) / 1e12
+    tiles = pa.pa_select_q_kernel(1, S, q_len, Hq, spec.num_kv_heads, dtype, L)
+    return {"us": round(us, 1), "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel": f"prefill_kernel<128,{tiles},single pass>" if tiles else "attend_kernel"}
 
 
 def load_traffic(workload, P):
@@ -372,6 +402,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         extras["v1_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 3, 1)
+        extras["prefill_q2048_L8192"] = prefill_extra(dev, stream, q.dtype, kcs[0], vcs[0], bt,
+                                                      spec, S, Hq, D)
 
     probe = None if args.no_probe else hbm_probe(dev)
 
