@@ -302,7 +302,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                 for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
             }
         }
-        uint4 pb[NCT];
+        // Values first (one masking branch), then per tile: weights, then its PV
+        // MFMAs, so the exponentials of tile ct + 1 can run while the matrix
+        // cores work on tile ct.
+        uint4 vv[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vv[t] = *reinterpret_cast<const uint4 *>(sv + 512 * t);
+        if (!full) {
+            // Value slots past the sequence end (or of a block not attended) are
+            // zeroed: their weights are 0, and 0 * NaN must not reach the sums.
+            const int keep = okb ? min(max(L - t0, 0), 8) : 0;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) vv[t] = keep_first(vv[t], keep);
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             float pr[2][4];
@@ -320,23 +332,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             }
             l[ct] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) +
                      ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
-            pb[ct] = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
-                                pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
+            const uint4 pb = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
+                                        pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[ct][t] = mfma_bf16_32(vv[t], pb, acc[ct][t]);
         }
-        uint4 vv[DT];
-#pragma unroll
-        for (int t = 0; t < DT; ++t) vv[t] = *reinterpret_cast<const uint4 *>(sv + 512 * t);
-        if (!full) {
-            // Value slots past the sequence end (or of a block not attended) are
-            // zeroed: their weights are 0, and 0 * NaN must not reach the sums.
-            const int keep = okb ? min(max(L - t0, 0), 8) : 0;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) vv[t] = keep_first(vv[t], keep);
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[ct][t] = mfma_bf16_32(vv[t], pb[ct], acc[ct][t]);
     };
 
     // Pipeline: the loads of step i + 2 are issued when step i starts, held in
