@@ -164,13 +164,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // Steps of two blocks; none without any cache block (every id would be skipped).
     const int nsteps = num_blocks > 0 ? (je_g - jb + 1) / 2 : 0;
 
-    float m[NCT], mt[NCT], l[NCT];  // reference max, true max (log2 units), lane's exp-sum share
+    float m[NCT], mt[NCT];  // reference max, true max (log2 units)
     f32x4 acc[NCT][DT];
+    // Exp-sums: one more PV MFMA per tile against an all-ones A operand leaves
+    // the column's sum of the (bf16) weights in every register of lane (n, q),
+    // so the sums cost no VALU additions and use the very weights the output
+    // does.
+    f32x4 accl[NCT];
+    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         m[ct] = -INFINITY;
         mt[ct] = -INFINITY;
-        l[ct] = 0.f;
+        accl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < DT; ++t) acc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                 const bool grow = mx2[ct] > m[ct] + kLazyLog2;
                 const float alpha = !grow ? 1.f : (m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - mx2[ct]));
                 if (grow) m[ct] = mx2[ct];
-                l[ct] *= alpha;
+                accl[ct] *= alpha;
 #pragma unroll
                 for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
             }
@@ -330,12 +336,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) pr[t][i] = dead ? 0.f : pr[t][i];
             }
-            l[ct] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) +
-                     ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
             const uint4 pb = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
                                         pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
 #pragma unroll
             for (int t = 0; t < DT; ++t) acc[ct][t] = mfma_bf16_32(vv[t], pb, acc[ct][t]);
+            accl[ct] = mfma_bf16_32(ones, pb, accl[ct]);
         }
     };
 
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // Results: lane (n, q) holds d = 16t + 4q + r of column cw + 16 ct + n.
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-        const float lc = column_sum(l[ct]);
+        const float lc = accl[ct][0];  // the column's exp-sum (all four registers hold it)
         const int c = cw + 16 * ct + n;
         if (c >= ncols) continue;
         const float inv = lc > 0.f ? 1.f / lc : 0.f;
