@@ -3,12 +3,11 @@ bandwidth probe libpa_probe.so in-tree.
 
     python split_kv_paged_pa_amd/build.py [-v]
 
-hipcc flags: gfx950 only, -O3, and packed-FP32 instructions disabled
+hipcc flags: gfx950 only, -O3, packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops) so that the compiler never
-emits v_pk_{add,mul,fma}_f32.  The decode kernels keep MFMA results in ordinary
-VGPRs (no AGPR copies around the VALU softmax code); the prefill kernel, whose
-accumulators outgrow the VGPRs, lets the compiler place them in AGPRs.  Each
-source is compiled to its own object, then linked.
+emits v_pk_{add,mul,fma}_f32, and MFMA results kept in ordinary VGPRs (no AGPR
+copies around the VALU softmax code).  Each source is compiled to its own
+object with its own flags, then linked.
 """
 import os
 import subprocess

@@ -46,10 +46,11 @@ hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hip
 int fused_merge_capacity();
 // n uint32 zeros at p (a plain fill kernel).
 hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t stream);
-// Many columns (G * qlen (query token, head) pairs per kv head), bf16 only: waves
-// of nct tiles of 16 columns each stream the blocks themselves.  parts == nullptr:
-// one pass over each sequence -> out; otherwise one workgroup per partition ->
-// partials (then launch_reduce).  nct is 1, 2 or 4.
+// Many columns (G * qlen (query token, head) pairs per kv head), bf16 only: each
+// wave holds nct tiles of 16 columns; a workgroup's 4 waves share one K/V stream
+// staged through LDS.  parts == nullptr: one pass over each sequence -> out;
+// otherwise one workgroup per partition -> partials (then launch_reduce).  nct is
+// 1, 2 or 4.
 hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, int nct,
                           hipStream_t stream);
 // Workgroups per kv head in grid y of launch_prefill.

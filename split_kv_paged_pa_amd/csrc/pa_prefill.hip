@@ -18,10 +18,14 @@
 //     every wave fetch a whole K/V block for only 16 columns of MFMA work, and
 //     the per-CU vector cache bandwidth, not the matrix cores, sets the speed.
 //     Here a wave owns NCT tiles of 16 columns (Q^T held in registers) and
-//     streams every block of its partition itself: each K/V operand loaded
-//     feeds NCT tiles.  The 4 waves of a workgroup take consecutive column
-//     groups of the same kv head and partition, so they read the same blocks
-//     close together in time and the cache serves three of the four.
+//     computes every block of its partition for them: each K/V operand it
+//     reads feeds NCT tiles.  The 4 waves of a workgroup take consecutive
+//     column groups of the same kv head and partition and share one K/V
+//     stream: each step of 32 tokens is fetched once by the whole workgroup
+//     (16 bytes x 4 per thread at D = 128), two steps ahead, into registers,
+//     then written to a 3-stage LDS ring, from which every wave reads its
+//     operands.  LDS positions are permuted at 16-byte granularity so that the
+//     8- and 16-lane groups of every operand read hit distinct banks.
 //   - MFMA v_mfma_f32_16x16x32_bf16 over steps of 32 tokens (two blocks).
 //     QK^T: A = keys (16 token rows x 32 d), B = Q^T (32 d x 16 columns).  The
 //     two 16-token tiles of a step take the tokens in an interleaved order --
@@ -30,14 +34,19 @@
 //     n: exactly the B operand P^T of the PV MFMA (k slot 8q+e = token 8q+e).
 //   - PV as O^T = V^T P^T: with values stored [D][16] per block, the A operand
 //     of lane (n, q) -- row d = 16t + n, tokens 8q .. 8q+7 -- is one contiguous
-//     16-byte load; keys, stored [D/8][16][8], are 16-byte loads as well.
+//     16-byte read; keys, stored [D/8][16][8], are 16-byte reads as well.
 //   - Online softmax in base 2 with a lazy reference: the weights are
 //     2^(z log2 e - m) with m the column's reference max, which moves only when
 //     a logit exceeds it by more than 2^8 (then the output and exp-sum are
 //     rescaled); weights stay below 256, the ratio output / exp-sum is what is
-//     kept, and the true max is tracked on the side for the partials.
-//   - The accumulators are the MFMA result registers (AGPRs when the register
-//     file needs them: this file is built without forcing VGPR results).
+//     kept, and the true max is tracked on the side for the partials.  The
+//     exp-sums come out of the PV step too: one more MFMA per tile with an
+//     all-ones A operand sums each column's bf16 weights.
+//   - A step issues its logits MFMAs, one (rarely taken) masking branch, one
+//     rescale branch for all tiles, then per tile the weights and their PV
+//     MFMAs: the common step is straight-line code.  Loop bounds and block ids
+//     stay in scalar registers, and MFMA results stay in VGPRs (no AGPR
+//     copies around the softmax code).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
