@@ -564,6 +564,38 @@ def test_prefill_long_sampled():
         assert_close(got[0, js], ref, "bf16", f"prefill long via {what}")
 
 
+def test_prefill_auto_batch():
+    """Twelve sequences of mixed length (some shorter than q_len, one empty),
+    q_len 48, GQA 8: the q_len entry points choose the prefill kernel on their
+    own (one column tile single pass, two split at P 512 on a 256-CU device) and
+    match the oracle."""
+    lens = [48, 3000, 0, 17, 640, 1200, 47, 2500, 96, 1, 2049, 777]
+    spec = wl.custom("prefill_auto_batch", 129, "bf16", 32, 4, 128, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q_len, P = 48, 512
+    q = _multi_query(spec, q_len)
+    _, kc, vc, bt, sl = b.numpy()
+    ref = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, spec.scale, dtype="bf16")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    k1 = pa.pa_select_q_kernel(1, len(lens), q_len, 32, 4, torch.bfloat16, db.max_seq_len)
+    k2 = pa.pa_select_q_kernel(0, len(lens), q_len, 32, 4, torch.bfloat16, db.max_seq_len, P)
+    print(f"[case] prefill auto batch: {cus} CUs, kernels v1 {k1} v2 {k2}", flush=True)
+    if cus == 256:
+        assert (k1, k2) == (1, 2)
+    o1 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v1_q(o1, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len)
+    assert_close(to_f64(o1), ref, "bf16", "auto batch v1_q")
+    ws = pa.new_workspace(len(lens), q_len * 32, 128, db.max_seq_len, P)
+    ws.view(torch.uint8).fill_(0xFF)
+    pa.pa_workspace_init(ws)
+    o2 = torch.full_like(q, float("nan"))
+    pa.pa_decode_v2_q(o2, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens,
+                      spec.scale, db.max_seq_len, P, ws)
+    assert_close(to_f64(o2), ref, "bf16", "auto batch v2_q")
+
+
 def test_graph_capture_replays():
     """The V2 step (two launches, no allocation, no memset) captured in a HIP graph:
     every replay, with eager work and synchronisations between replays, matches the
