@@ -707,6 +707,85 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Phase 2 for many rows with few partitions (q_len * Hq rows of a prefill-like
+// batch): one wave per (row, sequence), four rows per workgroup.  The wave takes
+// the row's partitions R at a time in increasing order -- max logits and
+// exp-sums through scalar loads, lane l holding d = l*DPL .. l*DPL + DPL - 1 of
+// each partial output -- and folds them with the Phase-2 rescale: M = max m_p,
+// w_p = exp(m_p - M) s_p, out = sum_p w_p o_p / sum_p w_p.
+// ---------------------------------------------------------------------------
+constexpr int kRowsPerGroup = 4;
+
+template <typename T, int D, int R>
+__global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
+    const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
+    const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_rows,
+    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    using M = Mma<T>;
+    constexpr int DPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.x * kRowsPerGroup + w;
+    if (h >= num_rows) return;  // no barrier in this kernel
+    const int s = blockIdx.y;
+    const size_t row = (size_t)s * num_rows + h;
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    const float *ml = max_logits + row * max_parts;
+    const float *es = exp_sums + row * max_parts;
+    const float *po = tmp_out + row * max_parts * D + lane * DPL;
+
+    float m_w = -INFINITY;  // running max
+    float wsum = 0.f;       // sum of exp(m_p - m_w) * s_p
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int p0 = 0; p0 < parts; p0 += R) {
+        float pm[R], ps[R], pv[R][DPL];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int p = p0 + r;
+            pm[r] = p < parts ? ml[p] : -INFINITY;
+            ps[r] = p < parts ? es[p] : 0.f;
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) pv[r][k] = p < parts ? po[(size_t)p * D + k] : 0.f;
+        }
+        float cm = pm[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) cm = fmaxf(cm, pm[r]);
+        if (cm > m_w) {  // wave-uniform
+            const float alpha = m_w == -INFINITY ? 0.f : exp_e(m_w - cm);
+            wsum *= alpha;
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) acc[k] *= alpha;
+            m_w = cm;
+        }
+        if (m_w == -INFINITY) continue;  // nothing valid yet
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (pm[r] != -INFINITY) {
+                const float wt = exp_e(pm[r] - m_w) * ps[r];
+                wsum += wt;
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) acc[k] += wt * pv[r][k];
+            }
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    T *orow = out + row * D + lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) orow[k] = M::from_float(acc[k] * inv);
+}
+
+// Phase 2 uses one wave per row when a row has few partitions (up to 16: one or
+// two rounds of loads), or when there are so many rows that one wave each still
+// fills the device and the partitions take a few rounds (up to 64); otherwise a
+// workgroup of 16 waves per row, whose waves load the partitions in parallel.
+constexpr int kRowReduceMaxParts = 16;
+constexpr long long kRowReduceManyRows = 8192;
+constexpr int kRowReduceManyRowsMaxParts = 64;
+
 __global__ void zero_words_kernel(uint32_t *__restrict__ p, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -749,6 +828,15 @@ hipError_t dispatch_attend(const Problem &pb, const Partials *parts, void *out, 
 template <typename T, int D>
 hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_heads, int max_seq_len,
                            const Partials &parts, void *out, hipStream_t stream) {
+    const long long rows = (long long)num_seqs * num_q_heads;
+    if (parts.max_parts <= kRowReduceMaxParts ||
+        (rows >= kRowReduceManyRows && parts.max_parts <= kRowReduceManyRowsMaxParts)) {
+        dim3 grid((num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, num_seqs);
+        reduce_rows_kernel<T, D, 8><<<grid, kRowsPerGroup * 64, 0, stream>>>(
+            parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
+            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+        return hipGetLastError();
+    }
     dim3 grid(num_q_heads, num_seqs);
     reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(parts.tmp_out, parts.exp_sums, parts.max_logits,
                                                   seq_lens, num_q_heads, max_seq_len,
