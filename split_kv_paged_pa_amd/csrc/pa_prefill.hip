@@ -222,9 +222,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             st[i] = *reinterpret_cast<const u32x4 *>(src);
         }
     };
-    // Values are stored with piece x (row x / 2, token half x % 2) at position
-    // x ^ ((x >> 4) & 1): the 16 lanes that read one half of rows 16t .. 16t+15
-    // then hit 16 different 16-byte bank groups.
     // LDS positions (16-byte units) inside a region, chosen so that every group
     // of 8 (and of 16) lanes of an operand read touches distinct banks:
     //   keys, piece (chunk c, token t) -> 16c + (t ^ 4 * (t / 8));
