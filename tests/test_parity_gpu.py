@@ -633,6 +633,41 @@ def test_graph_capture_replays():
         assert torch.equal(out.view(torch.int16), expect.view(torch.int16)), f"replay {rep}"
 
 
+def test_graph_capture_replays_prefill():
+    """The split q_len path on the prefill kernel and the one-wave-per-row reduce,
+    captured in a HIP graph: every replay matches the eager result bit for bit."""
+    spec = wl.custom("graph_prefill", 130, "bf16", 32, 4, 128, [3000, 700, 48])
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    q_len, P = 48, 512
+    assert pa.pa_select_q_kernel(0, 3, q_len, 32, 4, torch.bfloat16, db.max_seq_len, P) > 0
+    qs = [_multi_query(spec, q_len)]
+    qs += [(qs[0] * 0.5).contiguous(), (qs[0] * -1.0).contiguous()]
+    q_buf = qs[0].clone()
+    out = torch.empty_like(q_buf)
+    ws = pa.new_workspace(3, q_len * 32, 128, db.max_seq_len, P)
+    args = (db.key_cache, db.value_cache, db.block_tables, db.seq_lens, spec.scale, db.max_seq_len, P)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm-up outside capture
+        pa.pa_decode_v2_q(out, q_buf, *args, ws, stream=stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        pa.pa_decode_v2_q(out, q_buf, *args, ws, stream=stream)
+    for rep in range(6):
+        q = qs[rep % 3]
+        q_buf.copy_(q)
+        expect = torch.full_like(q, float("nan"))
+        pa.pa_decode_v2_q(expect, q, *args, pa.new_workspace(3, q_len * 32, 128, db.max_seq_len, P))
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), expect.view(torch.int16)), f"replay {rep}"
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads at full size.
 # ---------------------------------------------------------------------------
