@@ -59,6 +59,15 @@ __device__ __forceinline__ s16x4 pack_bf16(float a, float b, float c, float d) {
 
 __device__ __forceinline__ s16x4 pack_bf16(f32x4 v) { return pack_bf16(v[0], v[1], v[2], v[3]); }
 
+// Non-temporal loads (the "nt" bit): for data read exactly once, which gains
+// nothing from being kept in the L2 or the last-level cache.
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ u32x2 load_nt(const u32x2 *p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.x, v.y}); }
 __device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
 
