@@ -130,10 +130,12 @@ def cpu_baseline(batch, budget_s):
 
 def hbm_probe(dev):
     """Achievable HBM read bandwidth (GB/s) for streaming and for random 4 KiB chunks,
-    measured with libpa_probe.so (no arithmetic): the ceiling Phase 1 can approach.
-    'random' reads 300000 chunks (1.2 GB) drawn from a 4 GiB buffer per launch, so
-    the 256 MB Infinity Cache cannot hold them; 'kernel_shape' reads the same chunks
-    with the attention kernels' 16-rows-by-64-bytes load shape."""
+    measured with libpa_probe.so (16-byte non-temporal loads, no arithmetic): the
+    ceiling Phase 1 can approach.  'random' reads 300000 chunks (1.2 GB) drawn from
+    a 4 GiB buffer per launch, so the 256 MB Infinity Cache cannot hold them, with
+    1 KiB contiguous per load instruction (the decode kernels' shape for keys);
+    'rows16x64' reads the same chunks 64 bytes of each of 16 rows per instruction
+    (a token-major block layout)."""
     from split_kv_paged_pa_amd import probe
     buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
     ids = torch.randperm((4 << 30) // 4096, generator=torch.Generator().manual_seed(0))
@@ -142,7 +144,7 @@ def hbm_probe(dev):
     for groups in (196, 392):
         res[f"random_4KiB_{groups}wg"] = round(
             probe.read_bandwidth(buf, ids, 4096, 4, groups, reps=5, shape=0), 1)
-        res[f"random_4KiB_{groups}wg_kernel_shape"] = round(
+        res[f"random_4KiB_{groups}wg_rows16x64"] = round(
             probe.read_bandwidth(buf, ids, 4096, 4, groups, reps=5, shape=1), 1)
     del buf, ids
     torch.cuda.empty_cache()

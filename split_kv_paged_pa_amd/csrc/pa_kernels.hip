@@ -655,11 +655,12 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
             pm[r] = -INFINITY;
             ps[r] = 0.f;
             if (p < parts) {
-                pm[r] = ml[p];
-                ps[r] = es[p];
+                // Partials are read once: non-temporal loads.
+                pm[r] = __builtin_nontemporal_load(ml + p);
+                ps[r] = __builtin_nontemporal_load(es + p);
                 const float *src = po + (size_t)p * D + lane * DPL;
 #pragma unroll
-                for (int k = 0; k < DPL; ++k) po_v[r][k] = src[k];
+                for (int k = 0; k < DPL; ++k) po_v[r][k] = __builtin_nontemporal_load(src + k);
             }
         }
         float cm = pm[0];
@@ -749,10 +750,12 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int p = p0 + r;
-            pm[r] = p < parts ? ml[p] : -INFINITY;
-            ps[r] = p < parts ? es[p] : 0.f;
+            // Partials are read once: non-temporal loads.
+            pm[r] = p < parts ? __builtin_nontemporal_load(ml + p) : -INFINITY;
+            ps[r] = p < parts ? __builtin_nontemporal_load(es + p) : 0.f;
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) pv[r][k] = p < parts ? po[(size_t)p * D + k] : 0.f;
+            for (int k = 0; k < DPL; ++k)
+                pv[r][k] = p < parts ? __builtin_nontemporal_load(po + (size_t)p * D + k) : 0.f;
         }
         float cm = pm[0];
 #pragma unroll

@@ -1,17 +1,19 @@
 // pa_probe.hip -- HBM read-bandwidth probe for gfx950 (measurement only; not part
 // of the attention ABI).  It reads memory with the same access shape as the
-// decode kernels -- 16-byte loads, one chunk of `chunk_bytes` per wave at a time,
-// several chunks in flight per wave -- and does no arithmetic beyond folding the
-// loaded words into one value per thread, so its bandwidth is the ceiling the
-// attention kernels can approach for the same chunk order.
+// decode kernels -- 16-byte non-temporal loads, one chunk of `chunk_bytes` per
+// wave at a time, several chunks in flight per wave -- and does no arithmetic
+// beyond folding the loaded words into one value per thread, so its bandwidth
+// is the ceiling the attention kernels can approach for the same chunk order.
 //
 //   pa_probe_read(base, chunk_ids, num_chunks, chunk_bytes, waves_per_group,
 //                 num_groups, shape, sink, stream)
 // Chunk k is at base + chunk_ids[k] * chunk_bytes (chunk_ids NULL: chunk k).
 // shape 0: each load instruction of a wave covers 1 KiB of contiguous bytes.
-// shape 1: the attention kernels' shape for a 4 KiB chunk seen as 16 rows of
-//          256 bytes: lane l reads 16 bytes of row l % 16 at byte 16 * (l / 16)
-//          + 64 * c of the row, so an instruction covers 64 bytes of each row.
+// shape 1: a 4 KiB chunk seen as 16 rows of 256 bytes (a token-major block):
+//          lane l reads 16 bytes of row l % 16 at byte 16 * (l / 16) + 64 * c of
+//          the row, so an instruction covers 64 bytes of each row.  (The decode
+//          kernels' split cache layout reads as shape 0: 1 KiB of keys, 512 B of
+//          values contiguous per instruction.)
 // The chunks are split evenly over num_groups workgroups of waves_per_group
 // waves; sink receives one uint32 per thread (num_groups * waves_per_group * 64).
 // Returns 0 on success, 1 for invalid arguments, 2 for a failed launch.
@@ -21,6 +23,13 @@
 namespace {
 
 constexpr int kInFlight = 4;  // chunks in flight per wave
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte non-temporal load, as the decode kernels read keys and values.
+__device__ __forceinline__ v4u ld(const uint4 *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+}
 
 template <int NC, int SHAPE>
 __global__ __launch_bounds__(1024) void probe_kernel(const uint4 *__restrict__ base,
@@ -34,7 +43,7 @@ __global__ __launch_bounds__(1024) void probe_kernel(const uint4 *__restrict__ b
     const int last = min(first + chunks_per_group, num_chunks);
     uint32_t acc = 0;
     for (int k0 = first + w; k0 < last; k0 += nw * kInFlight) {
-        uint4 r[kInFlight][NC];
+        v4u r[kInFlight][NC];
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u) {
             const int k = k0 + u * nw;
@@ -42,17 +51,17 @@ __global__ __launch_bounds__(1024) void probe_kernel(const uint4 *__restrict__ b
             if (SHAPE == 0) {
                 const uint4 *p = base + (size_t)id * (NC * 64) + lane;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) r[u][c] = p[c * 64];
+                for (int c = 0; c < NC; ++c) r[u][c] = ld(p + c * 64);
             } else {
                 const uint4 *p = base + (size_t)id * (NC * 64) + (lane & 15) * (NC * 4) + (lane >> 4);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) r[u][c] = p[c * 4];
+                for (int c = 0; c < NC; ++c) r[u][c] = ld(p + c * 4);
             }
         }
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
 #pragma unroll
-            for (int c = 0; c < NC; ++c) acc ^= r[u][c].x ^ r[u][c].y ^ r[u][c].z ^ r[u][c].w;
+            for (int c = 0; c < NC; ++c) acc ^= r[u][c][0] ^ r[u][c][1] ^ r[u][c][2] ^ r[u][c][3];
     }
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
