@@ -614,7 +614,18 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 // same rescale as Phase 1.  The waves then merge through LDS in a fixed order,
 // so the result is reproducible bit for bit.  For up to NW * R partitions this
 // is a single round of global loads.
+//
+// The R loads of a round are straight-line code into distinct registers: an
+// index past the last partition is clamped to it (a row the wave has just
+// requested, so no extra memory traffic) and its values are masked after the
+// loads, so no branch separates the loads and all R are in flight together.
+// (With a branch per partition the compiler waited for each load before issuing
+// the next: one memory round trip per partition.)
 // ---------------------------------------------------------------------------
+template <int DPL> struct RowPiece;
+template <> struct RowPiece<1> { typedef float type; };
+template <> struct RowPiece<2> { typedef float type __attribute__((ext_vector_type(2))); };
+
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
@@ -623,6 +634,7 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     using M = Mma<T>;
     constexpr int NT = NW * 64;
     constexpr int DPL = D / 64;
+    typedef typename RowPiece<DPL>::type Piece;
     constexpr int R = 8;  // partitions in flight per wave
     __shared__ float sm_m[NW];
     __shared__ float sm_w[NW];
@@ -640,7 +652,7 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
     const float *ml = max_logits + head * max_parts;
     const float *es = exp_sums + head * max_parts;
-    const float *po = tmp_out + head * max_parts * D;
+    const Piece *po = reinterpret_cast<const Piece *>(tmp_out + head * max_parts * D) + lane;
 
     float m_w = -INFINITY;  // wave-local running max
     float wsum = 0.f;       // wave-local sum of exp(m_p - m_w) * s_p
@@ -648,20 +660,23 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
 #pragma unroll
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
     for (int p0 = w; p0 < parts; p0 += R * NW) {
-        float pm[R], ps[R], po_v[R][DPL];
+        float pm[R], ps[R];
+        Piece pv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int p = p0 + r * NW;
-            pm[r] = -INFINITY;
-            ps[r] = 0.f;
-            if (p < parts) {
-                // Partials are read once: non-temporal loads.
-                pm[r] = __builtin_nontemporal_load(ml + p);
-                ps[r] = __builtin_nontemporal_load(es + p);
-                const float *src = po + (size_t)p * D + lane * DPL;
+            const int p = min(p0 + r * NW, parts - 1);
+            pm[r] = ml[p];
+            ps[r] = es[p];
+            // Partial outputs are read once: non-temporal loads.
+            pv[r] = __builtin_nontemporal_load(po + (size_t)p * (D / DPL));
+        }
+        // Keep every load of the round ahead of the fold (the compiler would
+        // otherwise sink loads into the branches that use them).
 #pragma unroll
-                for (int k = 0; k < DPL; ++k) po_v[r][k] = __builtin_nontemporal_load(src + k);
-            }
+        for (int r = 0; r < R; ++r) asm volatile("" ::"s"(pm[r]), "s"(ps[r]), "v"(pv[r]));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (p0 + r * NW >= parts) pm[r] = -INFINITY;  // a clamped repeat
         }
         float cm = pm[0];
 #pragma unroll
@@ -679,8 +694,9 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
             if (pm[r] != -INFINITY) {
                 const float wt = exp_e(pm[r] - m_w) * ps[r];
                 wsum += wt;
+                const float *v = reinterpret_cast<const float *>(&pv[r]);
 #pragma unroll
-                for (int k = 0; k < DPL; ++k) acc[k] += wt * po_v[r][k];
+                for (int k = 0; k < DPL; ++k) acc[k] += wt * v[k];
             }
         }
     }
@@ -738,7 +754,8 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
     const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
     const float *ml = max_logits + row * max_parts;
     const float *es = exp_sums + row * max_parts;
-    const float *po = tmp_out + row * max_parts * D + lane * DPL;
+    typedef typename RowPiece<DPL>::type Piece;
+    const Piece *po = reinterpret_cast<const Piece *>(tmp_out + row * max_parts * D) + lane;
 
     float m_w = -INFINITY;  // running max
     float wsum = 0.f;       // sum of exp(m_p - m_w) * s_p
@@ -746,16 +763,23 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
 #pragma unroll
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
     for (int p0 = 0; p0 < parts; p0 += R) {
-        float pm[R], ps[R], pv[R][DPL];
+        float pm[R], ps[R];
+        Piece pv[R];
+        // As in reduce_kernel: straight-line loads, an index past the last
+        // partition clamped to it, its values masked after the loads.
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int p = p0 + r;
-            // Partials are read once: non-temporal loads.
-            pm[r] = p < parts ? __builtin_nontemporal_load(ml + p) : -INFINITY;
-            ps[r] = p < parts ? __builtin_nontemporal_load(es + p) : 0.f;
+            const int p = min(p0 + r, parts - 1);
+            pm[r] = ml[p];
+            ps[r] = es[p];
+            // Partial outputs are read once: non-temporal loads.
+            pv[r] = __builtin_nontemporal_load(po + (size_t)p * (D / DPL));
+        }
 #pragma unroll
-            for (int k = 0; k < DPL; ++k)
-                pv[r][k] = p < parts ? __builtin_nontemporal_load(po + (size_t)p * D + k) : 0.f;
+        for (int r = 0; r < R; ++r) asm volatile("" ::"s"(pm[r]), "s"(ps[r]), "v"(pv[r]));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (p0 + r >= parts) pm[r] = -INFINITY;  // a clamped repeat
         }
         float cm = pm[0];
 #pragma unroll
@@ -773,8 +797,9 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
             if (pm[r] != -INFINITY) {
                 const float wt = exp_e(pm[r] - m_w) * ps[r];
                 wsum += wt;
+                const float *v = reinterpret_cast<const float *>(&pv[r]);
 #pragma unroll
-                for (int k = 0; k < DPL; ++k) acc[k] += wt * pv[r][k];
+                for (int k = 0; k < DPL; ++k) acc[k] += wt * v[k];
             }
         }
     }
