@@ -334,7 +334,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "kernel": "attend_kernel<bf16,128,4,3,kPartials> (V2 Phase 1)",
+                "kernel": "attend_kernel<bf16,128,4,2,kPartials> (V2 Phase 1)",
                 "launch_us_mean": round(p1_us, 2),
                 "launch_us_p10_p90_single": [round(float(np.percentile(durs, 10)), 2),
                                              round(float(np.percentile(durs, 90)), 2)],

@@ -825,8 +825,11 @@ __global__ void zero_words_kernel(uint32_t *__restrict__ p, int n) {
 constexpr int kWaves = 4;
 constexpr int kReduceWaves = 16;
 
-// Blocks in flight per wave: three when a block's K and V fit in 32 VGPRs.
-template <typename T, int D> constexpr int prefetch_depth() { return D * sizeof(T) <= 256 ? 3 : 2; }
+// Ring slots per wave: the block being attended and the next one in flight.
+// (Three slots -- two blocks ahead -- measured 0.5-1.4% slower on MI355X: at
+// 194 VGPRs against 162 they leave two waves per SIMD instead of three, and a
+// CU streaming one workgroup gains nothing from the deeper ring.)
+template <typename T, int D> constexpr int prefetch_depth() { return 2; }
 
 template <typename T, int D, int MODE>
 hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hipStream_t stream) {
