@@ -70,10 +70,12 @@ def test_many_partitions_reduce_chunks():
 
 
 GROUPED = [  # S * Hkv * ceil(max_len / P) between one and four units per compute unit
+    # (on 256 CUs: 2, 3, 4, 4 and 4 partitions per workgroup)
     ("one_seq_p512", [20000], 8, 512),
     ("one_seq_p256", [20000], 8, 256),
     ("ragged_p256", [20000, 5, 13000], 4, 256),
     ("ragged_p1024", [100000, 17, 65536, 1], 2, 1024),
+    ("one_seq_100k_p512", [100000], 4, 512),
 ]
 
 
