@@ -1,0 +1,52 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU contract, the algorithmic
+byte count behind the roofline figure, and the source hash that ties the
+recorded traffic counters to the kernels they were taken on."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+from split_kv_paged_pa_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_bench_refuses_more_than_one_gpu():
+    env = {k: v for k, v in os.environ.items() if k not in ("WORLD_SIZE", "RANK", "LOCAL_RANK")}
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line for a configuration it does not run
+
+
+def test_phase1_bytes_by_hand():
+    """100000 tokens x 4 kv heads x 128 x 2 bytes x (K, V); the bf16 query (32 x 128);
+    6250 table entries and one seq_len (int32); the partials, 130 floats per (head,
+    partition): 98 partitions at P = 1024, 196 at P = 512."""
+    b = _bench()
+    spec = wl.config("long_100k_gqa8")
+    kv = 100000 * 4 * 128 * 2 * 2
+    rest = 32 * 128 * 2 + 6250 * 4 + 4
+    assert b.phase1_bytes(spec, 1024) == (kv + rest + 98 * 32 * 130 * 4, kv)
+    assert b.phase1_bytes(spec, 512) == (kv + rest + 196 * 32 * 130 * 4, kv)
+    assert kv == spec.kv_bytes == 204_800_000
+
+
+def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    b = _bench()
+    src = tmp_path / "k.hip"
+    monkeypatch.setattr(b, "KERNEL_SRC", [str(src)])
+    src.write_text("int f(int x) { return x + 1; }\n")
+    h0 = b.kernel_sha()
+    src.write_text("// a comment\nint f(int x) {  /* another */ return x + 1; }\n")
+    assert b.kernel_sha() == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert b.kernel_sha() != h0
