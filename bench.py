@@ -24,6 +24,7 @@ import json
 import os
 import re
 import statistics
+import subprocess
 import sys
 import time
 
@@ -126,6 +127,22 @@ def cpu_baseline(batch, budget_s):
             "kind": "oracle",
             "sample": f"{reps} full step(s) of {spec.name} (all {spec.num_q_heads} heads, "
                       f"{int(spec.seq_lens.sum())} tokens) in fp64 C, {el:.1f} s"}
+
+
+def device_info():
+    """Name, ISA, compute units and current clocks (rocm-smi, when it answers)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "clocks": None}
+    try:
+        r = subprocess.run(["/opt/rocm/bin/rocm-smi", "--showclocks", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        cards = json.loads(r.stdout)
+        card = cards[sorted(k for k in cards if k.startswith("card"))[0]]
+        info["clocks"] = {k.strip(" :"): v for k, v in card.items() if "clk" in k.lower()}
+    except Exception:  # no rocm-smi, no answer or another format: clocks stay unknown
+        pass
+    return info
 
 
 def hbm_probe(dev):
@@ -416,8 +433,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2), "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
-        "data": "synthetic (seeded N(0,1) bf16 keys/values/query, random block permutation)",
-        "config": {"workload": spec.name, "num_seqs": S, "seq_len": int(spec.seq_lens[0]),
+        "data": f"synthetic (seeded N(0,1) {spec.dtype} keys/values/query, random block permutation)",
+        "config": {"workload": spec.name, "num_seqs": S, "seq_len": int(spec.seq_lens.max()),
+                   "total_tokens": int(spec.seq_lens.sum()),
                    "q_heads": Hq, "kv_heads": spec.num_kv_heads, "head_dim": D, "block_size": 16,
                    "partition_size": P, "variant": args.variant, "kv_copies": len(kcs),
                    "kv_bytes_per_step": spec.kv_bytes},
@@ -428,6 +446,7 @@ def main():
         "hbm_probe": probe,
         "extras": extras,
         "device": torch.cuda.get_device_name(0),
+        "device_info": device_info(),
         "kernel_sha": kernel_sha(),
     }
     print(json.dumps(line), flush=True)
