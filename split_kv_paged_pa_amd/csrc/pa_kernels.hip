@@ -763,6 +763,106 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Phase 2 split over the output: workgroup (h * D/32 + x, s) of four waves
+// computes out[s][h][32x .. 32x+31] (rows and slices share grid x, whose limit
+// is 2^31 - 1: the q_len entry points give Phase 2 q_len * Hq rows).  Lane (j, c) of wave w -- j = lane / 8, c = lane % 8
+// -- takes d = 32x + 4c .. 4c+3 of partitions p = 8w + j + 32k, four per round.
+// Every wave first takes the global max M = max_p m_p over all the row's
+// partitions (so no lane ever rescales), then each lane sums
+// w_p = exp(m_p - M) s_p and w_p o_p[d .. d+3] over its partitions; the sums
+// are folded over j with a fixed butterfly, then over the four waves in order
+// through LDS, and out = sum / W.  Spreading a row over D/32 workgroups on
+// different CUs keeps each CU's load queue short: with one 16-wave workgroup
+// per row, the row's partials all pass one CU, and its fourth wave per SIMD
+// received them 0.75 us after its first.
+// ---------------------------------------------------------------------------
+constexpr int kSplitCols = 32;  // output floats per workgroup
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reduce_split_kernel(
+    const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
+    const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
+    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    using M = Mma<T>;
+    constexpr int K = 4;  // partitions per lane per round: 4 waves x 8 slots x K = 128
+    __shared__ __attribute__((aligned(16))) f32x4 sm_acc[4][8];
+    __shared__ float sm_w[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane >> 3;
+    const int c = lane & 7;
+    constexpr int kSlices = D / kSplitCols;
+    const int h = blockIdx.x / kSlices;
+    const int x = blockIdx.x - h * kSlices;
+    const int s = blockIdx.y;
+    const size_t head = (size_t)s * num_q_heads + h;
+    const int d0 = x * kSplitCols + 4 * c;
+
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    const float *ml = max_logits + head * max_parts;
+    const float *es = exp_sums + head * max_parts;
+    const float *po = tmp_out + head * max_parts * D + d0;
+
+    // Global max over the row's partitions, four loads per lane per round.
+    float mx = -INFINITY;
+    for (int p0 = 0; p0 < parts; p0 += 4 * 64) {
+        float m4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m4[i] = ml[min(p0 + lane + 64 * i, parts - 1)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, m4[i]);  // clamped repeats change no max
+    }
+    const float mg = wave_max(mx);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int b = 0; b < parts; b += 32 * K) {
+        const int p0 = b + 8 * w + j;
+        float pm[K], ps[K];
+        f32x4 pv[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int p = min(p0 + 32 * k, parts - 1);  // a clamped repeat is masked below
+            pm[k] = ml[p];
+            ps[k] = es[p];
+            pv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(po + (size_t)p * D));
+        }
+        // Keep the round's loads ahead of the fold (no load sunk into its branch).
+#pragma unroll
+        for (int k = 0; k < K; ++k) asm volatile("" ::"v"(pm[k]), "v"(ps[k]), "v"(pv[k]));
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (p0 + 32 * k < parts && pm[k] != -INFINITY) {
+                const float wt = exp_e(pm[k] - mg) * ps[k];
+                wsum += wt;
+                acc += wt * pv[k];
+            }
+        }
+    }
+    // Fold the eight partition slots of each d chunk: lanes c, c + 8, ..., c + 56.
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+        wsum += __shfl_xor(wsum, off);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], off);
+    }
+    if (j == 0) sm_acc[w][c] = acc;
+    if (lane == 0) sm_w[w] = wsum;
+    __syncthreads();
+    if (w == 0 && lane < 8) {
+        const f32x4 a = ((sm_acc[0][lane] + sm_acc[1][lane]) + sm_acc[2][lane]) + sm_acc[3][lane];
+        const float W = ((sm_w[0] + sm_w[1]) + sm_w[2]) + sm_w[3];
+        // W == 0 only for L == 0 or when no block id of the sequence was valid.
+        const float inv = W > 0.f ? 1.f / W : 0.f;
+        T *orow = out + head * D + x * kSplitCols + 4 * lane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) orow[r] = M::from_float(a[r] * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 2 for many rows with few partitions (q_len * Hq rows of a prefill-like
 // batch): one wave per (row, sequence), four rows per workgroup.  The wave takes
 // the row's partitions R at a time in increasing order -- max logits and
@@ -846,9 +946,15 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
 
 // Phase 2 uses one wave per row when a row has few partitions (up to 16: one or
 // two rounds of loads), or when there are so many rows that one wave each still
-// fills the device and the partitions take a few rounds (up to 64); otherwise a
-// workgroup of 16 waves per row, whose waves load the partitions in parallel.
+// fills the device and the partitions take a few rounds (up to 64); otherwise,
+// for fewer than kSplitMaxRows rows, D/32 four-wave workgroups per row
+// (reduce_split_kernel), and for more, a workgroup of 16 waves per row whose
+// waves load the partitions in parallel.
 constexpr int kRowReduceMaxParts = 16;
+// Below this many rows Phase 2 splits each row over D/32 workgroups (measured on
+// MI355X: the 100K-token step -0.4 to -1.0 us, 320-512 rows unchanged; at 4096
+// rows with 128 partitions the per-row workgroup is 0.9% faster).
+constexpr long long kSplitMaxRows = 2048;
 constexpr long long kRowReduceManyRows = 8192;
 constexpr int kRowReduceManyRowsMaxParts = 64;
 
@@ -906,11 +1012,19 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
             parts.partition_size, parts.max_parts, static_cast<T *>(out));
         return hipGetLastError();
     }
-    dim3 grid(num_q_heads, num_seqs);
-    reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(parts.tmp_out, parts.exp_sums, parts.max_logits,
-                                                  seq_lens, num_q_heads, max_seq_len,
-                                                  parts.partition_size, parts.max_parts,
-                                                  static_cast<T *>(out));
+    constexpr int kSlices = D / kSplitCols;
+    if (rows < kSplitMaxRows && (long long)num_q_heads * kSlices <= 0x7fffffffLL) {
+        // D/32 four-wave workgroups per row, on different CUs.
+        dim3 grid((unsigned)num_q_heads * kSlices, num_seqs);
+        reduce_split_kernel<T, D><<<grid, 256, 0, stream>>>(
+            parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
+            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+    } else {  // many rows: one 16-wave workgroup per row already spreads over the CUs
+        dim3 grid(num_q_heads, num_seqs);
+        reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(
+            parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
+            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+    }
     return hipGetLastError();
 }
 
