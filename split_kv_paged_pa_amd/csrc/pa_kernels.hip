@@ -805,6 +805,20 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
     const float *es = exp_sums + head * max_parts;
     const float *po = tmp_out + head * max_parts * D + d0;
 
+    // The first round's partials are requested together with the max logits of
+    // the global max: one memory round trip for up to 128 partitions.
+    float pm[K], ps[K];
+    f32x4 pv[K];
+    auto load_round = [&](int b) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int p = min(b + 8 * w + j + 32 * k, parts - 1);  // clamped repeats are masked
+            pm[k] = ml[p];
+            ps[k] = es[p];
+            pv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(po + (size_t)p * D));
+        }
+    };
+    if (parts > 0) load_round(0);
     // Global max over the row's partitions, four loads per lane per round.
     float mx = -INFINITY;
     for (int p0 = 0; p0 < parts; p0 += 4 * 64) {
@@ -819,19 +833,11 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int b = 0; b < parts; b += 32 * K) {
-        const int p0 = b + 8 * w + j;
-        float pm[K], ps[K];
-        f32x4 pv[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int p = min(p0 + 32 * k, parts - 1);  // a clamped repeat is masked below
-            pm[k] = ml[p];
-            ps[k] = es[p];
-            pv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(po + (size_t)p * D));
-        }
+        if (b > 0) load_round(b);
         // Keep the round's loads ahead of the fold (no load sunk into its branch).
 #pragma unroll
         for (int k = 0; k < K; ++k) asm volatile("" ::"v"(pm[k]), "v"(ps[k]), "v"(pv[k]));
+        const int p0 = b + 8 * w + j;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (p0 + 32 * k < parts && pm[k] != -INFINITY) {
