@@ -765,8 +765,10 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
 // ---------------------------------------------------------------------------
 // Phase 2 split over the output: workgroup (h * D/32 + x, s) of four waves
 // computes out[s][h][32x .. 32x+31] (rows and slices share grid x, whose limit
-// is 2^31 - 1: the q_len entry points give Phase 2 q_len * Hq rows).  Lane (j, c) of wave w -- j = lane / 8, c = lane % 8
-// -- takes d = 32x + 4c .. 4c+3 of partitions p = 8w + j + 32k, four per round.
+// is 2^31 - 1: the q_len entry points give Phase 2 q_len * Hq rows).  Lane
+// (j, c) of wave w -- j = lane / 8, c = lane % 8 -- takes d = 32x + 4c .. 4c+3
+// of partitions p = 8w + j + 32k, K per round (32 K partitions per round: K = 4,
+// or 8 for more than 128 partitions).
 // Every wave first takes the global max M = max_p m_p over all the row's
 // partitions (so no lane ever rescales), then each lane sums
 // w_p = exp(m_p - M) s_p and w_p o_p[d .. d+3] over its partitions; the sums
@@ -778,13 +780,12 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kSplitCols = 32;  // output floats per workgroup
 
-template <typename T, int D>
+template <typename T, int D, int K>
 __global__ __launch_bounds__(256) void reduce_split_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
     int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
     using M = Mma<T>;
-    constexpr int K = 4;  // partitions per lane per round: 4 waves x 8 slots x K = 128
     __shared__ __attribute__((aligned(16))) f32x4 sm_acc[4][8];
     __shared__ float sm_w[4];
     const int tid = threadIdx.x;
@@ -1022,9 +1023,14 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
     if (rows < kSplitMaxRows && (long long)num_q_heads * kSlices <= 0x7fffffffLL) {
         // D/32 four-wave workgroups per row, on different CUs.
         dim3 grid((unsigned)num_q_heads * kSlices, num_seqs);
-        reduce_split_kernel<T, D><<<grid, 256, 0, stream>>>(
-            parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
-            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+        if (parts.max_parts <= 128)
+            reduce_split_kernel<T, D, 4><<<grid, 256, 0, stream>>>(
+                parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads,
+                max_seq_len, parts.partition_size, parts.max_parts, static_cast<T *>(out));
+        else  // one round of loads for up to 256 partitions
+            reduce_split_kernel<T, D, 8><<<grid, 256, 0, stream>>>(
+                parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads,
+                max_seq_len, parts.partition_size, parts.max_parts, static_cast<T *>(out));
     } else {  // many rows: one 16-wave workgroup per row already spreads over the CUs
         dim3 grid(num_q_heads, num_seqs);
         reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(
