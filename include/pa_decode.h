@@ -26,6 +26,12 @@
  *   - caller-owned, pre-allocated V2 intermediates: commit 490ff98
  *     (paged_attn.py), "Three changes", item 2.
  *
+ * Deployment note: every call launches one or two short kernels whose first
+ * instruction reads its arguments.  Run the process with the ROCm runtime
+ * variable HIP_FORCE_DEV_KERNARG=1 (read when HIP starts) so that kernel
+ * arguments live in device memory: measured on MI355X, a 100K-token V2 step
+ * takes about 2 us less than with the default host-memory arguments.
+ *
  * Layouts (row-major, contiguous, all in device memory):
  *   query, out      [num_seqs][num_q_heads][head_dim]                         dtype
  *   key_cache       [num_blocks][num_kv_heads][head_dim / x][block_size][x]    dtype
