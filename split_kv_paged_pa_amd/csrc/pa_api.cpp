@@ -159,6 +159,7 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     parts->partition_size = partition_size;
     parts->max_parts = lay.max_parts;
     parts->per_group = partitions_per_group((long long)num_seqs * num_kv_heads * lay.max_parts);
+    parts->entry_parts = 1;
     return PA_OK;
 }
 
@@ -329,8 +330,16 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
                                   max_blocks_per_seq, max_seq_len, scale, dtype);
     if (parts.max_parts > 0) {
-        st = from_hip(tiles > 0 ? pa::launch_prefill(pb, &parts, nullptr, tiles, hs)
-                                : pa::launch_partitions(pb, parts, hs));
+        if (tiles > 0) {
+            st = from_hip(pa::launch_prefill(pb, &parts, nullptr, tiles, hs));
+        } else if (want_out && parts.per_group > 1 && parts.per_group <= pa::grouped_max_parts()) {
+            // Workgroups with several partitions fold them and write one group
+            // partial each; Phase 2 merges those.
+            st = from_hip(pa::launch_grouped(pb, parts, hs));
+            parts.entry_parts = parts.per_group;
+        } else {
+            st = from_hip(pa::launch_partitions(pb, parts, hs));
+        }
         if (st != PA_OK || !want_out) return st;
     }
     if (!want_out) return PA_OK;

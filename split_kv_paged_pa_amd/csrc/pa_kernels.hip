@@ -141,6 +141,9 @@ template <> struct Mma<float> {
 };
 
 constexpr int kMergeCap = 2048;  // group partials (heads x groups) one fused merge can weigh
+// Partitions one kGrouped workgroup can hold (per-partition wave states in LDS:
+// 4 x 4 waves x 16 columns x 132 floats = 132 KiB at D = 128, of gfx950's 160 KiB).
+constexpr int kMaxGroupedParts = 4;
 
 // Buffer descriptors for 16-byte stores: word 3 of a raw (untyped) buffer on
 // CDNA3/4, and the cache-policy bit of a device-scope write-through store (sc1).
@@ -245,8 +248,21 @@ __device__ __forceinline__ void merge_groups(const float *__restrict__ tmp_out,
 //     and writes the output.
 //   kSinglePass (V1): workgroup (0, kv head, sequence) covers the whole sequence
 //     as a single partition and writes the output.
+//   kGrouped (V2 Phase 1 when a workgroup takes several partitions, at most
+//     kMaxGroupedParts): the same partitions, each computed and merged across the
+//     waves exactly as in kPartials and folded, in order, into one group partial
+//     per head with the Phase-2 rescale (as kFused does); the workgroup writes
+//     that group partial -- normalised like a partition partial, with its exp-sum
+//     and max logit -- to entry blockIdx.x of the workspace, and Phase 2 merges
+//     ceil(parts / ppw) entries per row.  At a partition boundary each wave only
+//     deposits its state {max, exp-sum, output} for that partition in LDS, with
+//     no barrier; the cross-wave merges and the fold run once, after the
+//     workgroup's last block.  Every close a workgroup made mid-stream used to
+//     stall its waves at three barriers while their loads ran one block ahead
+//     (measured on the 100K-token workload: ~0.5-0.9 us per close), and its
+//     stores were ~0.7 us more.
 // ---------------------------------------------------------------------------
-enum Mode { kSinglePass = 0, kPartials = 1, kFused = 2 };
+enum Mode { kSinglePass = 0, kPartials = 1, kFused = 2, kGrouped = 3 };
 
 template <typename T, int D, int NW, int U, int MODE>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
@@ -257,6 +273,10 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
     T *__restrict__ out) {
     constexpr bool kFinal = MODE == kSinglePass;
+    // kFused folds each partition into the workgroup's group partial at its close;
+    // kGrouped deposits per-partition wave states (KP slots) and folds at the end.
+    constexpr bool kFold = MODE == kFused;
+    constexpr int KP = MODE == kGrouped ? kMaxGroupedParts : 1;
     using M = Mma<T>;
     constexpr int E = M::E;
     using VU = typename M::VU;
@@ -264,16 +284,21 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     constexpr int NT = D / 16;               // d tiles: value units and accumulator tiles
     constexpr int LDS_STRIDE = D + 4;
 
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
-    __shared__ float sm_f[NW][16];
-    __shared__ __attribute__((aligned(16))) float sm_o[NW][16][LDS_STRIDE];  // rows 16-byte aligned
+    // Per (partition slot, wave, column) states: max, exp-sum, merge factor, output.
+    __shared__ float sm_m[KP][NW][16];
+    __shared__ float sm_l[KP][NW][16];
+    __shared__ float sm_f[KP][NW][16];
+    __shared__ __attribute__((aligned(16))) float sm_o[KP][NW][16][LDS_STRIDE];  // rows 16-byte aligned
     // kFused: the group partial {max, exp-sum, unnormalised output} per head.
-    constexpr int GA = MODE == kFused ? 16 : 1;
+    constexpr int GA = kFold ? 16 : 1;
     __shared__ float sm_gm[GA];
     __shared__ float sm_gw[GA];
     __shared__ float sm_gs[GA];  // rescale of sm_ga for the partition being folded in
-    __shared__ __attribute__((aligned(16))) float sm_ga[GA][MODE == kFused ? D : 1];
+    __shared__ __attribute__((aligned(16))) float sm_ga[GA][kFold ? D : 1];
+    // kGrouped: rescale of the group partial before partition slot k is folded in,
+    // and the group's exp-sum.
+    __shared__ float sm_ks[KP][16];
+    __shared__ float sm_kw[MODE == kGrouped ? 16 : 1];
     __shared__ uint32_t sm_ticket;
 
     const int lane = threadIdx.x & 63;
@@ -319,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             return;
         }
     }
-    if (MODE == kFused) {
+    if (kFold) {
         for (int idx = threadIdx.x; idx < 16 * D; idx += NW * 64) sm_ga[idx / D][idx % D] = 0.f;
         if (threadIdx.x < 16) {
             sm_gm[threadIdx.x] = -INFINITY;
@@ -469,33 +494,66 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             attend(std::true_type{}, j, kr, vr);
     };
 
-    // End of partition p: merge the waves' states (fixed order) and write.
+    // One 16-byte write-through store (buffer_store_dwordx4 ... sc1) per thread of
+    // o at float d of row row_of(gg): whole cache lines, a quarter of the store
+    // instructions of one float per thread, and no dirty L2 lines at the end of
+    // the kernel.  A buffer store takes a wave-uniform base, so the lanes' rows
+    // are taken one at a time (two per wave at D = 128, four at D = 64); the
+    // descriptor spans one row.  Measured on MI355X against one float per thread:
+    // the 100K-token step -0.16 to -0.6 us, batches unchanged; plain 16-byte
+    // stores cost a batch with 42 MB of partials 4.6% at the kernel's end, and 4-
+    // or 8-byte stores in this mapping, which cover part of every line they
+    // touch, cost a 64-sequence batch 9%.
+    auto store_row4 = [&](auto row_of, int gg, int d, f32x4 o) {
+        typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+        for (bool pending = true; pending;) {
+            const int g0 = __builtin_amdgcn_readfirstlane(gg);
+            if (gg == g0) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4v, o),
+                    __builtin_amdgcn_make_buffer_rsrc(row_of(g0), 0, D * (int)sizeof(float),
+                                                      kBufferWord3),
+                    4 * d, 0, kCachePolicySc1);
+                pending = false;
+            }
+        }
+    };
+
+    // End of partition p: merge the waves' states (fixed order) and write (or,
+    // kFold, fold them into the group partial).  kGrouped: deposit this wave's
+    // state in partition slot p - p_begin, without a barrier (merged at the end).
     auto finish = [&](int p) {
         const float l_col = column_sum(l_run);
-        __syncthreads();  // the previous partition's readers are done with the LDS
+        const int k = MODE == kGrouped ? p - p_begin : 0;
+        if (MODE != kGrouped) __syncthreads();  // the previous partition's readers are done
         // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of head g.
         if (grp == 0) {
-            sm_m[w][g] = m_run;
-            sm_l[w][g] = l_col;
+            sm_m[k][w][g] = m_run;
+            sm_l[k][w][g] = l_col;
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4 *>(&sm_o[w][g][16 * t + 4 * grp]) = acc[t];
+            *reinterpret_cast<f32x4 *>(&sm_o[k][w][g][16 * t + 4 * grp]) = acc[t];
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (MODE == kGrouped) return;
         __syncthreads();
         // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
         if (threadIdx.x < 16) {
             const int gg = threadIdx.x;
             float mx = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[ww][gg]);
+            for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[0][ww][gg]);
             float f[NW];
             float total = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[ww][gg] - mx);
-                total += f[ww] * sm_l[ww][gg];
+                f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[0][ww][gg] - mx);
+                total += f[ww] * sm_l[0][ww][gg];
             }
-            if (MODE == kFused) {
+            if (kFold) {
                 // Fold (mx, total, sum_w f_w o_w) into the group partial with the
                 // Phase-2 rescale: weights exp(m - M') against the new group max M'.
                 const float gm = sm_gm[gg];
@@ -506,11 +564,11 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 sm_gw[gg] = sm_gw[gg] * a + total * b;
                 sm_gs[gg] = a;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * b;
+                for (int ww = 0; ww < NW; ++ww) sm_f[0][ww][gg] = f[ww] * b;
             } else {
                 const float inv = total > 0.f ? 1.f / total : 0.f;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) sm_f[ww][gg] = f[ww] * inv;
+                for (int ww = 0; ww < NW; ++ww) sm_f[0][ww][gg] = f[ww] * inv;
                 if (!kFinal && gg < ncol) {
                     const size_t row = qrow_of(gg) * max_parts + p;
                     store_through(exp_sums + row, total);
@@ -519,17 +577,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             }
         }
         __syncthreads();
-        // Each thread merges 4 consecutive d of one column, and a partition's
-        // output goes out as one 16-byte write-through store per thread
-        // (buffer_store_dwordx4 ... sc1): whole cache lines, a quarter of the
-        // store instructions of one float per thread, and no dirty L2 lines at
-        // the end of the kernel.  Measured on MI355X against one float per
-        // thread: the 100K-token step -0.16 to -0.6 us (the stores of a close
-        // cost about 0.7 us of streaming per close a workgroup makes
-        // mid-stream), batches unchanged; plain 16-byte stores cost a batch
-        // with 42 MB of partials 4.6% at the kernel's end, and 4- or 8-byte
-        // stores in this mapping, which cover part of every line they touch,
-        // cost a 64-sequence batch 9%.
+        // Each thread merges 4 consecutive d of one column; a partition's output
+        // goes out with store_row4.
         constexpr int C4 = D / 4;
         for (int idx = threadIdx.x; idx < ncol * C4; idx += NW * 64) {
             const int gg = idx / C4;
@@ -537,36 +586,18 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww)
-                o += sm_f[ww][gg] * *reinterpret_cast<const f32x4 *>(&sm_o[ww][gg][d]);
-            if (MODE == kFused) {
+                o += sm_f[0][ww][gg] * *reinterpret_cast<const f32x4 *>(&sm_o[0][ww][gg][d]);
+            if (kFold) {
                 f32x4 &ga = *reinterpret_cast<f32x4 *>(&sm_ga[gg][d]);
                 ga = ga * sm_gs[gg] + o;  // same thread owns (gg, d .. d+3) every time
             } else if (kFinal) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[qrow_of(gg) * D + d + r] = M::from_float(o[r]);
             } else {
-                // A buffer store takes a wave-uniform base: the lanes' rows are
-                // taken one at a time (two per wave at D = 128, four at D = 64),
-                // each store at byte 4 d of its row; the descriptor spans one row.
-                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                for (bool pending = true; pending;) {
-                    const int g0 = __builtin_amdgcn_readfirstlane(gg);
-                    if (gg == g0) {
-                        float *row = tmp_out + (qrow_of(g0) * max_parts + p) * D;
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4v, o),
-                            __builtin_amdgcn_make_buffer_rsrc(row, 0, D * (int)sizeof(float),
-                                                              kBufferWord3),
-                            4 * d, 0, kCachePolicySc1);
-                        pending = false;
-                    }
-                }
+                store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + p) * D; },
+                           gg, d, o);
             }
         }
-        m_run = -INFINITY;
-        l_run = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
     // ---- attend side: consume the ring in order; close each partition when the
@@ -598,6 +629,65 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         if (done) break;
     }
     while (a_p < p_end) finish(a_p++);
+
+    if (MODE == kGrouped) {
+        // Merge each partition's deposited wave states across the waves and fold
+        // the partitions, in order, into the group partial -- per column, the
+        // same arithmetic as the kFused close: M' = max(M, m_p), W = W a + s_p b
+        // with a = exp(M - M'), b = exp(m_p - M') -- then write it, normalised,
+        // to entry blockIdx.x of the row.
+        const int np = p_end - p_begin;  // 1 .. KP, uniform
+        __syncthreads();
+        if (threadIdx.x < 16) {
+            const int gg = threadIdx.x;
+            float gm = -INFINITY, gw = 0.f;
+            for (int k = 0; k < np; ++k) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[k][ww][gg]);
+                float f[NW];
+                float total = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[k][ww][gg] - mx);
+                    total += f[ww] * sm_l[k][ww][gg];
+                }
+                const float gm_new = fmaxf(gm, mx);
+                const float a = gm == -INFINITY ? 0.f : exp_e(gm - gm_new);
+                const float b = mx == -INFINITY ? 0.f : exp_e(mx - gm_new);
+                gw = gw * a + total * b;
+                gm = gm_new;
+                sm_ks[k][gg] = a;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) sm_f[k][ww][gg] = f[ww] * b;
+            }
+            sm_kw[gg] = gw;
+            if (gg < ncol) {
+                const size_t row = qrow_of(gg) * max_parts + blockIdx.x;
+                store_through(exp_sums + row, gw);
+                store_through(max_logits + row, gm);
+            }
+        }
+        __syncthreads();
+        constexpr int C4 = D / 4;
+        for (int idx = threadIdx.x; idx < ncol * C4; idx += NW * 64) {
+            const int gg = idx / C4;
+            const int d = (idx - gg * C4) * 4;
+            f32x4 ga = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < np; ++k) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww)
+                    o += sm_f[k][ww][gg] * *reinterpret_cast<const f32x4 *>(&sm_o[k][ww][gg][d]);
+                ga = ga * sm_ks[k][gg] + o;
+            }
+            const float W = sm_kw[gg];
+            ga = ga * (W > 0.f ? 1.f / W : 0.f);
+            store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + blockIdx.x) * D; },
+                       gg, d, ga);
+        }
+        return;
+    }
     if (MODE != kFused) return;
 
     // ---- kFused epilogue.  Group partial g of this workgroup goes to entry gi =
@@ -607,8 +697,11 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __syncthreads();
     // Publication: the group partial is stored with device-scope atomic stores
     // (written through to the device's point of coherence), each wave waits until
-    // its stores have completed, and only then is the ticket taken.  No cache
-    // writeback is needed: nothing else this workgroup wrote is read elsewhere.
+    // its stores have completed, the workgroup barrier orders them before thread
+    // 0's ticket, and the ticket is an acquire-release read-modify-write at device
+    // scope: the last workgroup's acquire then synchronises with every earlier
+    // workgroup's release, so the merge reads complete group partials under the
+    // memory model, not only on this hardware's store ordering.
     if (threadIdx.x < group) {
         const size_t row = (head0 + threadIdx.x) * max_parts + gi;
         __hip_atomic_store(exp_sums + row, sm_gw[threadIdx.x], __ATOMIC_RELAXED,
@@ -628,7 +721,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __syncthreads();
     uint32_t *ticket = tickets + (size_t)s * num_kv_heads + kvh;
     if (threadIdx.x == 0)
-        sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int parts = (nblk + bp - 1) / bp;
     const int n = (parts + ppw - 1) / ppw;  // workgroups of this (sequence, kv head) with work
@@ -1009,10 +1102,20 @@ hipError_t dispatch_attend(const Problem &pb, const Partials *parts, void *out, 
 
 template <typename T, int D>
 hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_heads, int max_seq_len,
-                           const Partials &parts, void *out, hipStream_t stream) {
+                           const Partials &in, void *out, hipStream_t stream) {
     const long long rows = (long long)num_seqs * num_q_heads;
-    if (parts.max_parts <= kRowReduceMaxParts ||
-        (rows >= kRowReduceManyRows && parts.max_parts <= kRowReduceManyRowsMaxParts)) {
+    // Entries of a row stand for entry_parts partitions each: the kernels count
+    // ceil(L / (P * entry_parts)) = ceil(ceil(L / P) / entry_parts) of them.  A
+    // span at or beyond max_seq_len is one entry per non-empty row, and is passed
+    // as max_seq_len so that it fits an int.
+    Partials parts = in;
+    const int ep = in.entry_parts > 1 ? in.entry_parts : 1;
+    const long long span = (long long)in.partition_size * ep;
+    if (ep > 1 && span >= max_seq_len) parts.partition_size = max_seq_len > 0 ? max_seq_len : 1;
+    else parts.partition_size = (int)span;
+    const int entries = (in.max_parts + ep - 1) / ep;  // most entries a row can hold
+    if (entries <= kRowReduceMaxParts ||
+        (rows >= kRowReduceManyRows && entries <= kRowReduceManyRowsMaxParts)) {
         dim3 grid((num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, num_seqs);
         reduce_rows_kernel<T, D, 8><<<grid, kRowsPerGroup * 64, 0, stream>>>(
             parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
@@ -1023,7 +1126,7 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
     if (rows < kSplitMaxRows && (long long)num_q_heads * kSlices <= 0x7fffffffLL) {
         // D/32 four-wave workgroups per row, on different CUs.
         dim3 grid((unsigned)num_q_heads * kSlices, num_seqs);
-        if (parts.max_parts <= 128)
+        if (entries <= 128)
             reduce_split_kernel<T, D, 4><<<grid, 256, 0, stream>>>(
                 parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads,
                 max_seq_len, parts.partition_size, parts.max_parts, static_cast<T *>(out));
@@ -1049,6 +1152,13 @@ hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream) 
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream) {
     return dispatch_attend<kPartials>(pb, &parts, nullptr, stream);
 }
+
+hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream) {
+    if (parts.per_group < 1 || parts.per_group > kMaxGroupedParts) return hipErrorInvalidValue;
+    return dispatch_attend<kGrouped>(pb, &parts, nullptr, stream);
+}
+
+int grouped_max_parts() { return kMaxGroupedParts; }
 
 hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hipStream_t stream) {
     return dispatch_attend<kFused>(pb, &parts, out, stream);

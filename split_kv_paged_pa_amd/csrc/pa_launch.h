@@ -31,14 +31,21 @@ struct Partials {
     float *max_logits;   // [S][Hq][max_parts]
     uint32_t *tickets;   // [S][Hkv] arrival counters of the fused form (zero between calls)
     int partition_size;
-    int max_parts;
+    int max_parts;   // entries per row of the three arrays (the row stride)
     int per_group;   // consecutive partitions handled by one Phase-1 workgroup
+    int entry_parts; // partitions behind each entry Phase 2 reads: 1 after launch_partitions,
+                     // per_group after launch_grouped
 };
 
 // V1: one workgroup per (kv head, sequence) over the whole sequence -> out.
 hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream);
 // V2 Phase 1: one workgroup per (partition, kv head, sequence) -> partials.
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream);
+// V2 Phase 1 with per_group > 1: the same grid; each workgroup folds its partitions
+// into one group partial (the Phase-2 rescale) and writes it to entry blockIdx.x
+// of the row -> Phase 2 then runs with entry_parts = per_group.
+hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream);
+int grouped_max_parts();  // largest per_group launch_grouped takes
 // V2 in one launch: the Phase-1 grid; each workgroup folds its partitions into a
 // group partial, and the last workgroup of each (sequence, kv head) merges them -> out.
 // Needs group * ceil(max_parts / per_group) <= fused_merge_capacity().
@@ -55,7 +62,8 @@ hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, i
                           hipStream_t stream);
 // Workgroups per kv head in grid y of launch_prefill.
 int prefill_column_groups(int group, int qlen, int nct);
-// V2 Phase 2: one workgroup per (query head, sequence): partials -> out.
+// V2 Phase 2: partials -> out.  Row r of sequence s holds ceil(ceil(L_s / P) /
+// entry_parts) valid entries (P = partition_size).
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
                          int max_seq_len, Dtype dtype, const Partials &parts, void *out,
                          hipStream_t stream);
