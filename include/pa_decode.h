@@ -155,15 +155,40 @@ pa_status_t pa_decode_v1(void *out, const void *query, const void *key_cache,
                          int max_seq_len, float scale, pa_dtype_t dtype, void *stream);
 
 /*
+ * Partition size for the split-KV entry points when the caller passes
+ * partition_size = 0.  The pages treat the partition size as the knob that
+ * trades Phase-1 parallelism against Phase-2 cost (commit 900ae0b, "Two
+ * changes based on CCCL source reading", item 1; commit 490ff98, "Three
+ * changes", item 3); their 512 and 1024 were chosen for a 16-SM device.  This
+ * rule is measured on MI355X: 2048 tokens, unless that gives fewer work units
+ * (num_seqs * num_kv_heads * ceil(max_seq_len / 2048)) than the current
+ * device has compute units; then the smallest multiple of 16 (at least 256)
+ * that gives at most one partition per compute unit, i.e. about
+ * max_seq_len * num_seqs * num_kv_heads / CUs (1568 for one 100000-token
+ * sequence with 4 kv heads on 256 CUs).  Returns 2048 for invalid arguments.
+ * Host-only; 256 compute units are assumed when no device is visible.  Size the
+ * workspace with the value it returns: pa_workspace_size(..., 0) is invalid.
+ */
+int pa_select_partition_size(int num_seqs, int num_kv_heads, int max_seq_len);
+
+/*
  * V2: split-KV.  Phase 1, one workgroup per (partition group, kv head,
- * sequence), writes each partition's partials into the workspace; Phase 2, one
- * workgroup per (query head, sequence), merges them into out (commit 15ef28e,
- * "[OPT] PagedAttention V2 implementation", Phase 1 and Phase 2).  Two
- * launches on `stream`, no host synchronisation.  workspace_bytes must be at
- * least pa_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
- * partition_size) and the workspace 16-byte aligned; it may be reused by later
- * calls on the same stream, but two calls in flight at once must not share it.
- * A sequence with L == 0 gets an all-zero output row.
+ * sequence), computes each partition's partials; Phase 2, one workgroup per
+ * (query head, sequence), merges them into out (commit 15ef28e, "[OPT]
+ * PagedAttention V2 implementation", Phase 1 and Phase 2).  Two launches on
+ * `stream`, no host synchronisation.  partition_size = 0 uses
+ * pa_select_partition_size(num_seqs, num_kv_heads, max_seq_len).
+ * workspace_bytes must be at least pa_workspace_size(num_seqs, num_q_heads,
+ * head_dim, max_seq_len, partition_size) and the workspace 16-byte aligned; it
+ * may be reused by later calls on the same stream, but two calls in flight at
+ * once must not share it.  A sequence with L == 0 gets an all-zero output row.
+ * When the partitions are few enough that one Phase-1 workgroup takes several
+ * consecutive partitions (up to 4), it merges them -- each partition computed
+ * and merged across its waves as in Phase 1, then folded in order with the
+ * Phase-2 rescale -- and the workspace entry that Phase 2 reads holds that
+ * group: after pa_decode_v2 the workspace therefore holds Phase-2 entries, not
+ * necessarily one per partition (pa_decode_v2_partials writes one per
+ * partition).
  */
 pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          const void *value_cache, const int32_t *block_tables,
@@ -216,7 +241,9 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
  * pa_decode_v1_q is the single pass.  pa_decode_v2_q is split-KV in two
  * launches; its workspace holds q_len * num_q_heads rows per sequence, i.e.
  * pa_workspace_size(num_seqs, q_len * num_q_heads, head_dim, max_seq_len,
- * partition_size) bytes.  With q_len = 1 they equal pa_decode_v1 and
+ * partition_size) bytes; partition_size = 0 uses
+ * pa_select_partition_size(num_seqs, num_kv_heads * ceil(G * q_len / 16),
+ * max_seq_len).  With q_len = 1 they equal pa_decode_v1 and
  * pa_decode_v2 bit for bit.
  */
 pa_status_t pa_decode_v1_q(void *out, const void *query, const void *key_cache,
@@ -286,8 +313,9 @@ int pa_select_q_kernel(int single_pass, int num_seqs, int q_len, int num_q_heads
                        pa_dtype_t dtype, int max_seq_len, int partition_size);
 
 /* V2 Phase 1 alone: fills the workspace partials (layout at pa_workspace_size)
- * for partitions p < ceil(L / partition_size) of each sequence; other entries
- * are not written.  Same arguments as pa_decode_v2, without out. */
+ * for partitions p < ceil(L / partition_size) of each sequence, one entry per
+ * partition; other entries are not written.  Same arguments as pa_decode_v2,
+ * without out (partition_size = 0 as there). */
 pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                   const void *value_cache, const int32_t *block_tables,
                                   const int32_t *seq_lens, int num_seqs, int num_q_heads,
@@ -299,7 +327,8 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
 /* V2 Phase 2 alone: merges the workspace partials into out with the
  * log-sum-exp rescale (commit 15ef28e, "[OPT] PagedAttention V2
  * implementation", Phase 2).  Reads only partitions p < ceil(L / partition_size)
- * of each sequence. */
+ * of each sequence, one entry per partition as pa_decode_v2_partials writes
+ * them.  partition_size must be the explicit size (0 is not accepted here). */
 pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
                                 int head_dim, int max_seq_len, pa_dtype_t dtype,
                                 int partition_size, const void *workspace, size_t workspace_bytes,

@@ -7,11 +7,13 @@ the same function names; `workloads` draws seeded synthetic decode batches.
 from .api import (PagedAttentionError, load_library, new_workspace, pa_decode, pa_decode_auto,
                   pa_decode_v1, pa_decode_v1_q, pa_decode_v2, pa_decode_v2_partials,
                   pa_decode_v2_q, pa_decode_v2_reduce,
-                  pa_decode_v2_single, pa_prefill_v1, pa_prefill_v2, pa_select_q_kernel, pa_select_v2, pa_select_v2_auto, pa_status_string,
+                  pa_decode_v2_single, pa_prefill_v1, pa_prefill_v2, pa_select_partition_size,
+                  pa_select_q_kernel, pa_select_v2, pa_select_v2_auto, pa_status_string,
                   pa_workspace_init, pa_workspace_layout, pa_workspace_size, workspace_views)
 
 __all__ = ["PagedAttentionError", "load_library", "new_workspace", "pa_decode", "pa_decode_auto",
            "pa_decode_v1", "pa_decode_v1_q", "pa_decode_v2", "pa_decode_v2_partials",
            "pa_decode_v2_q", "pa_decode_v2_reduce",
-           "pa_decode_v2_single", "pa_prefill_v1", "pa_prefill_v2", "pa_select_q_kernel", "pa_select_v2", "pa_select_v2_auto", "pa_status_string",
+           "pa_decode_v2_single", "pa_prefill_v1", "pa_prefill_v2", "pa_select_partition_size",
+           "pa_select_q_kernel", "pa_select_v2", "pa_select_v2_auto", "pa_status_string",
            "pa_workspace_init", "pa_workspace_layout", "pa_workspace_size", "workspace_views"]

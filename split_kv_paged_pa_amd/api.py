@@ -7,7 +7,7 @@ call raises.
 
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
-pa_workspace_layout, pa_workspace_init, pa_select_v2, pa_select_v2_auto,
+pa_workspace_layout, pa_workspace_init, pa_select_partition_size, pa_select_v2, pa_select_v2_auto,
 pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_prefill_v1,
 pa_prefill_v2, pa_select_q_kernel, pa_status_string.
 """
@@ -57,6 +57,8 @@ def load_library():
     lib.pa_workspace_init.restype = I
     lib.pa_select_v2.argtypes = [I, I, I, I]
     lib.pa_select_v2.restype = I
+    lib.pa_select_partition_size.argtypes = [I, I, I]
+    lib.pa_select_partition_size.restype = I
     lib.pa_select_v2_auto.argtypes = [I, I, I, I]
     lib.pa_select_v2_auto.restype = I
     lib.pa_decode_auto.argtypes = [P] + common + [I, P, Z, P]
@@ -113,6 +115,11 @@ def pa_workspace_init(workspace, stream=None):
     """Zero the counter header of a workspace (needed once, before its first pa_decode_v2)."""
     wp, wb = _workspace(workspace)
     _check(load_library().pa_workspace_init(wp, wb, _stream(stream)), "pa_workspace_init")
+
+
+def pa_select_partition_size(num_seqs: int, num_kv_heads: int, max_seq_len: int) -> int:
+    """The partition size the split-KV entry points use for partition_size = 0."""
+    return int(load_library().pa_select_partition_size(num_seqs, num_kv_heads, max_seq_len))
 
 
 def pa_select_v2(max_seq_len: int, num_seqs: int, num_kv_heads: int, partition_size: int) -> bool:

@@ -35,6 +35,18 @@ constexpr long long kTicketSlots = (long long)(kHeaderBytes / sizeof(uint32_t));
 constexpr int kGroupFewUnits = 4;
 constexpr int kMaxDevices = 64;
 
+// Partition size the library picks (partition_size = 0): measured on MI355X over
+// the 100K-token sequence (32/4 heads), 16 ragged sequences up to 32K tokens, 64
+// ragged sequences up to 131K tokens and 8 x 131K tokens (GQA 5), at P = 256 ..
+// 16384: 2048 is within 2% of the best size on every batch (1024 ties, 4096
+// loses up to 2x on the 64-sequence batch, 256 and 512 lose 3-20%); when
+// (sequence, kv head) pairs are so few that 2048-token partitions give fewer
+// work units than compute units, one partition per compute unit is faster (the
+// 100K-token step at P = 1568: 39.4 us against 39.9 us at 2048 and 40.4 us at
+// 1024).
+constexpr int kAutoPartition = 2048;
+constexpr int kAutoPartitionMin = 256;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Compute units of the current device (cached per device; 0 if unknown).
@@ -262,6 +274,22 @@ pa_status_t pa_workspace_init(void *workspace, size_t workspace_bytes, void *str
                                           static_cast<hipStream_t>(stream)));
 }
 
+int pa_select_partition_size(int num_seqs, int num_kv_heads, int max_seq_len) {
+    if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return kAutoPartition;
+    int cus = compute_units();
+    if (cus <= 0) cus = 256;
+    const long long pairs = (long long)num_seqs * num_kv_heads;
+    const long long units = pairs * (((long long)max_seq_len + kAutoPartition - 1) / kAutoPartition);
+    if (units >= cus) return kAutoPartition;
+    // pairs < cus here: k partitions per pair make at most one unit per compute unit.
+    const long long k = cus / pairs;
+    long long p = ((long long)max_seq_len + k - 1) / k;
+    p = (p + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
+    if (p < kAutoPartitionMin) p = kAutoPartitionMin;
+    if (p > kAutoPartition) p = kAutoPartition;
+    return (int)p;
+}
+
 int pa_select_v2(int max_seq_len, int num_seqs, int num_kv_heads, int partition_size) {
     (void)num_seqs;
     (void)num_kv_heads;
@@ -317,6 +345,8 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
     if (rows_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     // Workgroups per (sequence, partition group): kv heads times column chunks.
     const int chunks = (int)(((long long)(num_q_heads / num_kv_heads) * q_len + 15) / 16);
+    if (partition_size == 0)
+        partition_size = pa_select_partition_size(num_seqs, num_kv_heads * chunks, max_seq_len);
     pa::Partials parts;
     st = carve(num_seqs, (int)rows_per_seq, num_kv_heads * chunks, head_dim, max_seq_len,
                partition_size, workspace, workspace_bytes, &parts);
@@ -440,6 +470,8 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                                    1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                    max_blocks_per_seq, max_seq_len, scale, dtype);
     if (st != PA_OK) return st;
+    if (partition_size == 0)
+        partition_size = pa_select_partition_size(num_seqs, num_kv_heads, max_seq_len);
     pa::Partials parts;
     st = carve(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
                workspace, workspace_bytes, &parts);

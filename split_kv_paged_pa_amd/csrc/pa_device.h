@@ -68,6 +68,30 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
 }
 __device__ __forceinline__ u32x2 load_nt(const u32x2 *p) { return __builtin_nontemporal_load(p); }
 
+// Buffer descriptor word 3 of a raw (untyped) buffer on CDNA3/4, and the
+// cache-policy bit of a device-scope write-through store (sc1).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCachePolicySc1 = 16;
+
+// Four consecutive output values base[4 i .. 4 i + 3] written through to the
+// device's point of coherence with one store (8 bytes of bf16 or 16 of float):
+// an output leaves no dirty L2 line behind for the end-of-kernel release to
+// write back.  base must be wave-uniform and 16-byte aligned; n = elements from
+// base the descriptor covers.
+__device__ __forceinline__ void store_out4(uint16_t *base, int n, int i, float a, float b, float c,
+                                           float d) {
+    const u32x2 v = {pack2_bf16(a, b), pack2_bf16(c, d)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, __builtin_amdgcn_make_buffer_rsrc(base, 0, 2 * n, kBufferWord3),
+                                          8 * i, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ void store_out4(float *base, int n, int i, float a, float b, float c,
+                                           float d) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(base, 0, 4 * n, kBufferWord3),
+                                           16 * i, 0, kCachePolicySc1);
+}
+
 __device__ __forceinline__ s16x4 lo_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.x, v.y}); }
 __device__ __forceinline__ s16x4 hi_half(uint4 v) { return __builtin_bit_cast(s16x4, u32x2{v.z, v.w}); }
 

@@ -42,6 +42,11 @@ class DeviceBatch:
         return out
 
     def workspace(self, P, poison=True):
+        """A workspace for partition size P (0: the library's choice, sized with the
+        value pa_select_partition_size returns)."""
+        if P == 0:
+            P = pa.pa_select_partition_size(self.spec.num_seqs, self.spec.num_kv_heads,
+                                            self.max_seq_len)
         ws = pa.new_workspace(self.spec.num_seqs, self.spec.num_q_heads, self.spec.head_dim,
                               self.max_seq_len, P)
         if poison:

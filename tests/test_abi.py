@@ -85,7 +85,7 @@ CASES = [
     ("head_dim 96", dict(D=96), UNSUP),
     ("block size 32", dict(bs=32), UNSUP),
     ("partition 24", dict(P=24), UNSUP),
-    ("partition 0", dict(P=0), UNSUP),
+    ("partition -16", dict(P=-16), UNSUP),
     ("too many seqs", dict(S=70000), UNSUP),
     ("workspace too small", dict(wsb=1000), WS),
     ("nan scale", dict(scale=math.nan), ARG),
@@ -154,6 +154,32 @@ def test_workspace_init_and_launch_count_checks():
     # 625 * 8 = 5000 (sequence, kv head) pairs, more than the 4096 header counters.
     big = (FAKE, FAKE, FAKE, FAKE, FAKE, 625, 64, 8, 128, 16, 100, 2048, 20000, 0.088, 1)
     assert lib.pa_decode_v2_single(FAKE, *big, 1024, FAKE, 1 << 40, None) == UNSUP
+
+
+def test_partition_size_rule():
+    """partition_size = 0: 2048 tokens, or one partition per compute unit when the
+    (sequence, kv head) pairs are few (no device here: 256 compute units)."""
+    import torch
+    if torch.cuda.is_available():
+        return  # the rule depends on the device's compute units
+    sel = pa.pa_select_partition_size
+    assert sel(1, 4, 100000) == 1568          # 4 x ceil(100000 / 1568) = 256 units
+    assert 4 * -(-100000 // 1568) == 256 and 4 * -(-100000 // 1552) > 256
+    assert sel(16, 8, 32768) == 2048          # 2048 units at 2048 tokens
+    assert sel(64, 8, 131072) == 2048
+    assert sel(8, 8, 131072) == 2048
+    assert sel(1, 8, 65536) == 2048           # exactly 256 units
+    assert sel(1, 8, 65535) == 2048
+    assert sel(1, 4, 8192) == 256             # 16 units at 2048: floor of 256 tokens
+    assert sel(1, 1, 1000) == 256
+    assert sel(0, 4, 100) == 2048 and sel(1, 4, 0) == 2048   # invalid: the default
+    # The workspace is sized with the chosen value; 0 itself is not a size.
+    assert pa.pa_workspace_size(1, 32, 128, 100000, 0) == 0
+    lib = pa.load_library()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, 4, 128, 16, 8192, 6250, 100000, 0.088, 1)
+    need = pa.pa_workspace_size(1, 32, 128, 100000, 1568)
+    assert lib.pa_decode_v2(*args, 0, FAKE, need - 1, None) == WS
+    assert lib.pa_decode_v2_reduce(FAKE, FAKE, 1, 32, 128, 100000, 1, 0, FAKE, need, None) == UNSUP
 
 
 def test_select_v2_auto_rule():

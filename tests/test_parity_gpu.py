@@ -671,11 +671,11 @@ def test_graph_capture_replays_prefill():
 
 # ---------------------------------------------------------------------------
 # The five named workloads at full size, every (sequence, head) row compared
-# with the oracle.  Partition sizes: the workload's own, plus 2048 for the
-# 100K-token sequence.
+# with the oracle.  Partition sizes: the workload's own, 0 (the library's
+# choice), plus 2048 for the 100K-token sequence.
 # ---------------------------------------------------------------------------
-FULL = [("tiny_f32_2k", ()), ("long_100k_gqa8", (2048,)), ("batch16_1k_32k", ()),
-        ("batch64_mixed_outliers", ()), ("batch8_131k_gqa5", ())]
+FULL = [("tiny_f32_2k", (0,)), ("long_100k_gqa8", (2048, 0)), ("batch16_1k_32k", (0,)),
+        ("batch64_mixed_outliers", (0,)), ("batch8_131k_gqa5", (0,))]
 
 
 @pytest.mark.parametrize("name,extra_P", FULL, ids=[f[0] for f in FULL])
@@ -694,6 +694,33 @@ def test_named_workload(name, extra_P):
         print(f"[case] {name}: {variant} P={P} max abs err {err:.3e}", flush=True)
     del db
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S,P", [(200, 256), (257, 512), (96, 4096)])
+def test_many_ragged_sequences(S, P):
+    """Many ragged sequences, zero-length ones among them: Phase 1's grid rotates
+    each row's partition index (rows whose length is a multiple of 8 included:
+    12 and 8 partitions at P = 256 and 4096).  Every row against the oracle, the
+    partials too."""
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 3000 if P < 4096 else 32768, size=S, endpoint=True)
+    lens[rng.integers(S, size=S // 8)] = 0
+    spec = wl.custom(f"many{S}", 132, "bf16", 8, 2, 64, lens)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    print(f"[case] many sequences S={S} P={P}", flush=True)
+    assert_close(to_f64(db.run_v2(P)), oracle_out(b), "bf16", f"many S={S} P={P}")
+    ws = db.workspace(P)
+    pa.pa_decode_v2_partials(*db.args(), P, ws)
+    tmp, es, ml = (to_f64(x) for x in pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads,
+                                                         spec.head_dim, db.max_seq_len, P))
+    q, kc, vc, bt, sl = b.numpy()
+    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P, dtype="bf16",
+                                     max_partitions=tmp.shape[2])
+    for s_, L in enumerate(sl):
+        n = oracle.num_partitions(L, P)
+        assert np.all(np.abs(ml[s_, :, :n] - rml[s_, :, :n]) <= 1e-5 * (1 + np.abs(rml[s_, :, :n])))
+        assert_close(tmp[s_, :, :n], rtmp[s_, :, :n], "bf16", f"partials s={s_}")
 
 
 def test_reduce_workgroup_per_row_all_rows():
