@@ -13,18 +13,25 @@ the cache pool is replicated `--copies` times and step i reads copy i mod
 copies: every step streams its keys and values from HBM.  Inputs are resident
 in HBM before the timed region starts.
 
-Prints one JSON line with the throughput (KV GB/s), the roofline of the
-dominant kernel (Phase 1) timed with HIP events on the launch stream, the HBM
-traffic measured by rocprofv3 counters when those were taken on the current
-kernel source (else null), and the CPU oracle timed on a bounded sample.
+Prints one JSON line:
+  - value / ms_per_step: the K timed steps of the headline form (V2 at
+    --partition-size), bracketed by torch.cuda.synchronize(), wall clock or HIP
+    events, whichever is longer;
+  - step_us: median, p10 and p90 of the same form from one event pair per step;
+  - variants: the same per-step statistics for V2 at P = 512, at the library's
+    partition size (partition_size = 0), and for V1;
+  - roofline: the dominant kernel -- Phase 1 exactly as the step runs it
+    (pa_decode_v2_groups) -- timed with HIP events on the launch stream, its
+    algorithmic bytes, and the HBM traffic measured by rocprofv3 counters when
+    those were taken on the current kernel source (else null);
+  - cpu_baseline: the fp64 CPU oracle on a bounded sample.
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
-import statistics
-import subprocess
 import sys
 import time
 
@@ -65,18 +72,39 @@ def kernel_sha():
     return hashlib.sha256("".join(src.split()).encode()).hexdigest()[:16]
 
 
-def phase1_bytes(spec, P):
+def phase1_bytes(spec, P, per_entry=1):
     """Algorithmic bytes of one Phase-1 launch: each K/V row of the actual tokens
     read once (Hkv*D*es*2 per token), the query, the block-table entries used,
-    seq_lens, and the partials written (D+2 floats per (seq, head, partition))."""
+    seq_lens, and the workspace entries written (D+2 floats per (seq, head,
+    entry); an entry stands for per_entry consecutive partitions)."""
     es = spec.elem_size
     lens = spec.seq_lens.astype(np.int64)
-    parts = int(np.sum(-(-lens // P)))
+    parts = -(-lens // P)
+    entries = int(np.sum(-(-parts // per_entry)))
     kv = int(lens.sum()) * spec.num_kv_heads * spec.head_dim * es * 2
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * es
     tables = int(np.sum(-(-lens // 16))) * 4 + spec.num_seqs * 4
-    partials = parts * spec.num_q_heads * (spec.head_dim + 2) * 4
+    partials = entries * spec.num_q_heads * (spec.head_dim + 2) * 4
     return kv + q + tables + partials, kv
+
+
+def step_stats(us):
+    """Median, p10 and p90 of per-step microseconds."""
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "n": len(us)}
+
+
+def time_per_step(run, n, stream):
+    """One event pair per step, n steps back to back: microseconds of each step
+    (the pair's own overhead included)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i].record(stream)
+        run(i)
+    ev[n].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
 
 
 def prefill_extra(dev, stream, dtype, kc, vc, bt, spec, S, Hq, D, q_len=2048, L=8192):
@@ -138,18 +166,23 @@ def cpu_baseline(batch, budget_s):
 
 
 def device_info():
-    """Name, ISA, compute units and current clocks (rocm-smi, when it answers)."""
+    """Name, ISA, compute units, and the current shader and memory clock levels
+    from the amdgpu driver's sysfs files when they are readable (no child
+    process is started from this GPU process)."""
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count, "clocks": None}
-    try:
-        r = subprocess.run(["/opt/rocm/bin/rocm-smi", "--showclocks", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        cards = json.loads(r.stdout)
-        card = cards[sorted(k for k in cards if k.startswith("card"))[0]]
-        info["clocks"] = {k.strip(" :"): v for k, v in card.items() if "clk" in k.lower()}
-    except Exception:  # no rocm-smi, no answer or another format: clocks stay unknown
-        pass
+    clocks = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+        try:
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if ln.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            card = path.split("/")[4]
+            clocks[f"{card}.{os.path.basename(path)[7:]}"] = cur[0]
+    info["clocks"] = clocks or None
     return info
 
 
@@ -181,11 +214,12 @@ DISPATCH_LENS = [512, 1024, 2048, 4096, 8192, 16384]
 
 
 def dispatch_sweep(dev):
-    """V1 against V2 (P = 512, 1024) and the two dispatch rules, over uniform-length
-    bf16 batches (Hq = 8 Hkv, D = 128, random block tables, random values).  Prints
-    one JSON object with a row per (S, Hkv, L): the measured us per call of each
-    form, and the us of the form pa_select_v2 (the pages' rule) and
-    pa_select_v2_auto (the MI355X rule) pick."""
+    """V1 against V2 (P = 512, 1024, and the library's choice) and the two dispatch
+    rules, over uniform-length bf16 batches (Hq = 8 Hkv, D = 128, random block
+    tables, random values).  Prints one JSON object with a row per (S, Hkv, L):
+    the measured us per call of each form, the partition size the library picks,
+    and the us of the form pa_select_v2 (the pages' rule) and pa_select_v2_auto
+    (the MI355X rule) pick."""
     G, D = 8, 128
     st = torch.cuda.current_stream()
     rows = []
@@ -201,9 +235,10 @@ def dispatch_sweep(dev):
             bt = torch.randperm(NB, device=dev, generator=gen).to(torch.int32).view(S, nblk)
             sl = torch.full((S,), L, dtype=torch.int32, device=dev)
             out = torch.empty_like(q)
-            row = {"S": S, "Hkv": Hkv, "L": L}
-            for name, P in (("v1", None), ("v2_p512", 512), ("v2_p1024", 1024)):
-                ws = None if P is None else pa.new_workspace(S, Hq, D, L, P, device=dev)
+            p_auto = pa.pa_select_partition_size(S, Hkv, L)
+            row = {"S": S, "Hkv": Hkv, "L": L, "auto_partition_size": p_auto}
+            for name, P in (("v1", None), ("v2_p512", 512), ("v2_p1024", 1024), ("v2_auto", 0)):
+                ws = None if P is None else pa.new_workspace(S, Hq, D, L, P or p_auto, device=dev)
 
                 def run():
                     if P is None:
@@ -221,7 +256,7 @@ def dispatch_sweep(dev):
                 torch.cuda.synchronize()
                 row[name] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
             row["pages_rule_us"] = row["v2_p1024"] if pa.pa_select_v2(L, S, Hkv, 1024) else row["v1"]
-            row["auto_rule_us"] = row["v2_p1024"] if pa.pa_select_v2_auto(L, S, Hkv, 1024) else row["v1"]
+            row["auto_rule_us"] = row["v2_auto"] if pa.pa_select_v2_auto(L, S, Hkv, 0) else row["v1"]
             print(f"[sweep] {row}", file=sys.stderr, flush=True)
             rows.append(row)
             del q, kc, vc, bt, sl, out
@@ -239,16 +274,18 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long_100k_gqa8")
-    ap.add_argument("--partition-size", type=int, default=1024)
+    ap.add_argument("--partition-size", type=int, default=1024,
+                    help="partition size of the headline form (0: the library's choice)")
     ap.add_argument("--variant", choices=["v2", "v1"], default="v2")
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other partition sizes and V1 (for short profiling passes)")
     ap.add_argument("--extras", action="store_true",
-                    help="also time V2 at other partition sizes, V2 in a single launch, V2 with "
-                         "several query tokens per sequence and V1 (same workload)")
-    ap.add_argument("--no-extras", action="store_true", help=argparse.SUPPRESS)
+                    help="also time V2 in a single launch, V2 with several query tokens per "
+                         "sequence, and the tiled prefill kernel (same cache)")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="instead of the step benchmark, time V1 / V2 over a grid of batch shapes "
                          "and compare the two dispatch rules")
@@ -268,9 +305,11 @@ def main():
         dispatch_sweep(dev)
         return
     spec = wl.config(args.workload)
-    P = args.partition_size
     batch = wl.generate(spec)
-    S, Hq, D = spec.num_seqs, spec.num_q_heads, spec.head_dim
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    L = spec.max_seq_len
+    P_auto = pa.pa_select_partition_size(S, Hkv, L)
+    P = args.partition_size or P_auto
     q = batch.query.to(dev)
     bt = batch.block_tables.to(dev)
     sl = batch.seq_lens.to(dev)
@@ -280,28 +319,49 @@ def main():
         kcs.append(kcs[0].clone())
         vcs.append(vcs[0].clone())
     out = torch.empty_like(q)
-    ws = pa.new_workspace(S, Hq, D, spec.max_seq_len, P, device=dev)
-    L = spec.max_seq_len
     stream = torch.cuda.current_stream()
+    workspaces = {}
 
-    def step(i, variant=args.variant, part=P, wsp=ws):
+    def workspace(part):
+        if part not in workspaces:
+            workspaces[part] = pa.new_workspace(S, Hq, D, L, part or P_auto, device=dev)
+        return workspaces[part]
+
+    def v2_calls(part):
+        """One pre-marshalled pa_decode_v2 per cache copy (partition_size part, 0 =
+        the library's choice)."""
+        return [pa.bind_decode_v2(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, part,
+                                  workspace(part), stream) for c in range(len(kcs))]
+
+    def v1_step(i):
         c = i % len(kcs)
-        if variant == "v2":
-            pa.pa_decode_v2(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, part, wsp)
-        else:
-            pa.pa_decode_v1(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L)
+        pa.pa_decode_v1(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L)
 
-    # Parity of the timed configuration on sampled rows, before any timing.
+    head = v2_calls(args.partition_size)
+
+    def step(i):
+        if args.variant == "v2":
+            head[i % len(head)]()
+        else:
+            v1_step(i)
+
+    # Parity of every timed form on sampled rows, before any timing.
     import oracle
-    step(0)
-    torch.cuda.synchronize()
     rows = np.array([(s, h) for s in range(S) for h in range(0, Hq, max(1, Hq // 8))], np.int32)
     ref = oracle.decode(*batch.numpy(), spec.scale, dtype=spec.dtype, rows=rows)
-    got = out.double().cpu().numpy()[rows[:, 0], rows[:, 1]]
-    err = np.abs(got - ref)
-    assert np.all(err <= 2e-2 + 1e-2 * np.abs(ref)), f"bench parity failed: {err.max()}"
-    print(f"[bench] parity on {len(rows)} rows: max abs err {err.max():.3e}", file=sys.stderr,
-          flush=True)
+    forms = [("headline", step)]
+    if not args.no_variants:
+        forms += [("v2_p512", lambda i, c=v2_calls(512): c[i % len(c)]()),
+                  ("v2_auto", lambda i, c=v2_calls(0): c[i % len(c)]()), ("v1", v1_step)]
+    for name, run in forms:
+        out.fill_(float("nan"))
+        run(0)
+        torch.cuda.synchronize()
+        got = out.double().cpu().numpy()[rows[:, 0], rows[:, 1]]
+        err = np.abs(got - ref)
+        assert np.all(err <= 2e-2 + 1e-2 * np.abs(ref)), f"bench parity failed ({name}): {err.max()}"
+        print(f"[bench] parity {name} on {len(rows)} rows: max abs err {err.max():.3e}",
+              file=sys.stderr, flush=True)
 
     # Calibration copy for the HBM counters: a plain 768 MiB device-to-device copy
     # (a size no other copy here has, so its dispatches are easy to pick out).
@@ -311,6 +371,7 @@ def main():
         cal_dst.copy_(cal_src)
     del cal_src, cal_dst
 
+    # The timed region: K steps between synchronisations.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -330,79 +391,75 @@ def main():
           f"(wall {ms_wall * 1e3:.2f}, events {ms_event * 1e3:.2f}), {value:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    # Dominant kernel alone (V2 Phase 1) on the launch stream: an event pair around
-    # n1 back-to-back launches gives the mean duration; one pair per launch gives the spread.
+    # Per-step statistics of the headline form, then of the other forms.
+    n_steps = max(20, min(args.steps, 100))
+    step_us = step_stats(time_per_step(step, n_steps, stream))
+
+    def form_line(run, n):
+        for i in range(5 if n > 5 else 1):
+            run(i)
+        st = step_stats(time_per_step(run, n, stream))
+        st["gb_per_s"] = round(spec.kv_bytes / (st["median"] * 1e-6) / 1e9, 1)
+        st["hbm_peak_frac"] = round(st["gb_per_s"] / HBM_PEAK_GBS, 4)
+        return st
+    variants = {}
+    if not args.no_variants:
+        variants["v2_p512"] = dict(form_line(forms[1][1], n_steps), partition_size=512)
+        variants["v2_auto"] = dict(form_line(forms[2][1], n_steps), partition_size=P_auto)
+        variants["v1"] = form_line(v1_step, 5)
+        for k, v in variants.items():
+            print(f"[bench] {k}: median {v['median']} us (p10 {v['p10']}, p90 {v['p90']})",
+                  file=sys.stderr, flush=True)
+
+    # Dominant kernel alone: V2 Phase 1 exactly as the step runs it.  An event pair
+    # around n1 back-to-back launches gives the mean duration; one pair per launch
+    # gives the spread.
+    wsh = workspace(args.partition_size)
+    per_entry = 1
+
+    def phase1(i):
+        nonlocal per_entry
+        c = i % len(kcs)
+        per_entry = pa.pa_decode_v2_groups(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, wsh)
     n1 = max(20, min(args.steps, 100))
     for i in range(5):
-        c = i % len(kcs)
-        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+        phase1(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record(stream)
     for i in range(n1):
-        c = i % len(kcs)
-        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
+        phase1(i)
     e1.record(stream)
     torch.cuda.synchronize()
     p1_us = e0.elapsed_time(e1) * 1e3 / n1
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(n1)]
-    for i, (a, b) in enumerate(pairs):
-        c = i % len(kcs)
-        a.record(stream)
-        pa.pa_decode_v2_partials(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws)
-        b.record(stream)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e3 for a, b in pairs]  # us, includes per-pair event overhead
-    alg_bytes, kv_bytes = phase1_bytes(spec, P)
+    durs = time_per_step(phase1, n1, stream)  # includes per-pair event overhead
+    alg_bytes, kv_bytes = phase1_bytes(spec, P, per_entry)
     achieved = alg_bytes / (p1_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, P)
+    mode = "kPartials" if per_entry == 1 else f"kGrouped, {per_entry} partitions per workgroup"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "kernel": "attend_kernel<bf16,128,4,2,kPartials> (V2 Phase 1)",
+                "kernel": f"attend_kernel<bf16,128,4,2,{mode}> (V2 Phase 1)",
                 "launch_us_mean": round(p1_us, 2),
                 "launch_us_p10_p90_single": [round(float(np.percentile(durs, 10)), 2),
                                              round(float(np.percentile(durs, 90)), 2)],
                 "algorithmic_bytes_per_launch": alg_bytes}
 
     extras = {}
-    if args.extras and not args.no_extras and args.variant == "v2":
-        for other in (512, 1024, 2048):
-            if other == P:
-                continue
-            ws2 = pa.new_workspace(S, Hq, D, L, other, device=dev)
-            for i in range(5):
-                step(i, "v2", other, ws2)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(50):
-                step(i, "v2", other, ws2)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / 50
-            extras[f"v2_p{other}_us_per_step"] = round(us, 2)
+    if args.extras and args.variant == "v2":
         ws1 = pa.new_workspace(S, Hq, D, L, P, device=dev)
 
         def single(i):
             c = i % len(kcs)
             pa.pa_decode_v2_single(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws1)
         try:
-            for i in range(5):
-                single(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(50):
-                single(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            extras[f"v2_single_launch_p{P}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 50, 2)
+            extras[f"v2_single_launch_p{P}_us_per_step"] = form_line(single, 50)["median"]
         except pa.PagedAttentionError as e:
             extras[f"v2_single_launch_p{P}_us_per_step"] = f"not applicable: {e}"
         # Several query tokens per sequence (causal over the cache): as many as fit the
         # 16 tile columns with this GQA group.
-        qlen = max(1, 16 // (Hq // spec.num_kv_heads))
+        qlen = max(1, 16 // (Hq // Hkv))
         if qlen > 1:
             qm = torch.randn(S, qlen, Hq, D, device=dev).to(q.dtype)
             om = torch.empty_like(qm)
@@ -411,24 +468,7 @@ def main():
             def multi(i):
                 c = i % len(kcs)
                 pa.pa_decode_v2_q(om, qm, kcs[c], vcs[c], bt, sl, spec.scale, L, P, wsq)
-            for i in range(5):
-                multi(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(50):
-                multi(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            extras[f"v2_qlen{qlen}_p{P}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 50, 2)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        step(0, "v1")
-        e0.record(stream)
-        for i in range(3):
-            step(i, "v1")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        extras["v1_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / 3, 1)
+            extras[f"v2_qlen{qlen}_p{P}_us_per_step"] = form_line(multi, 50)["median"]
         extras["prefill_q2048_L8192"] = prefill_extra(dev, stream, q.dtype, kcs[0], vcs[0], bt,
                                                       spec, S, Hq, D)
 
@@ -444,9 +484,11 @@ def main():
         "data": f"synthetic (seeded N(0,1) {spec.dtype} keys/values/query, random block permutation)",
         "config": {"workload": spec.name, "num_seqs": S, "seq_len": int(spec.seq_lens.max()),
                    "total_tokens": int(spec.seq_lens.sum()),
-                   "q_heads": Hq, "kv_heads": spec.num_kv_heads, "head_dim": D, "block_size": 16,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": 16,
                    "partition_size": P, "variant": args.variant, "kv_copies": len(kcs),
                    "kv_bytes_per_step": spec.kv_bytes},
+        "step_us": step_us,
+        "variants": variants,
         # Phase 2 and the gap between the launches, as the step sees them.
         "phase2_us_in_step": round(ms_per_step * 1e3 - p1_us, 2),
         "roofline": roofline,

@@ -47,6 +47,9 @@
  * dtype (PA_DTYPE_F32 or PA_DTYPE_BF16) applies to query, caches and out.
  * Partials in the V2 workspace are always float32 (layout below).
  *
+ * Alignment: query, key_cache, value_cache, out and the workspace must be
+ * 16-byte aligned (else PA_ERR_INVALID_ARGUMENT).
+ *
  * Ownership and threading.  Every pointer is caller-owned device memory (except
  * host-side size outputs).  The library never allocates, frees or synchronises,
  * and never reads device memory from the host.  It holds no state: calls from
@@ -323,6 +326,34 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                   int max_blocks_per_seq, int max_seq_len, float scale,
                                   pa_dtype_t dtype, int partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* V2 Phase 1 alone, exactly as pa_decode_v2 runs it: one workspace entry per
+ * partition, or, when workgroups take several consecutive partitions, one
+ * entry per such group (each partition computed and merged across the waves as
+ * in Phase 1, the group's partitions then folded in order with the Phase-2
+ * rescale; same layout and meaning as a partition's entry, over the group's
+ * tokens).  *partitions_per_entry (may be NULL) receives the number of
+ * partitions behind each entry (1, or 2 to 4), which
+ * pa_decode_v2_reduce_entries takes.  Same arguments as pa_decode_v2, without
+ * out; partition_size = 0 as there.  pa_decode_v2 is this call followed by
+ * pa_decode_v2_reduce_entries, bit for bit. */
+pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_seq_len, float scale,
+                                pa_dtype_t dtype, int partition_size, void *workspace,
+                                size_t workspace_bytes, int *partitions_per_entry, void *stream);
+
+/* V2 Phase 2 over entries that stand for partitions_per_entry (>= 1)
+ * consecutive partitions each, as pa_decode_v2_groups writes them: reads the
+ * ceil(ceil(L / partition_size) / partitions_per_entry) entries of each row.
+ * partitions_per_entry < 1 gives PA_ERR_INVALID_ARGUMENT. */
+pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int num_seqs,
+                                        int num_q_heads, int head_dim, int max_seq_len,
+                                        pa_dtype_t dtype, int partition_size,
+                                        int partitions_per_entry, const void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /* V2 Phase 2 alone: merges the workspace partials into out with the
  * log-sum-exp rescale (commit 15ef28e, "[OPT] PagedAttention V2

@@ -6,7 +6,8 @@ no fallback: if the library is missing or the tensors are not on a GPU, the
 call raises.
 
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
-pa_decode_v2_partials, pa_decode_v2_reduce, pa_workspace_size,
+pa_decode_v2_partials, pa_decode_v2_reduce, pa_decode_v2_groups,
+pa_decode_v2_reduce_entries, pa_workspace_size,
 pa_workspace_layout, pa_workspace_init, pa_select_partition_size, pa_select_v2, pa_select_v2_auto,
 pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_prefill_v1,
 pa_prefill_v2, pa_select_q_kernel, pa_status_string.
@@ -86,6 +87,10 @@ def load_library():
     lib.pa_decode_v2_partials.restype = I
     lib.pa_decode_v2_reduce.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
     lib.pa_decode_v2_reduce.restype = I
+    lib.pa_decode_v2_groups.argtypes = common + [I, P, Z, ctypes.POINTER(I), P]
+    lib.pa_decode_v2_groups.restype = I
+    lib.pa_decode_v2_reduce_entries.argtypes = [P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.pa_decode_v2_reduce_entries.restype = I
     _lib = lib
     return lib
 
@@ -227,6 +232,27 @@ def pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, sca
            "pa_decode_v2")
 
 
+def bind_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                   partition_size, workspace, stream=None):
+    """pa_decode_v2 with its arguments checked and marshalled once: returns a
+    callable that enqueues the call again (for launch loops, where re-marshalling
+    the tensors each time would cost more host time than the launch itself).  The
+    library still checks every call; the tensors must stay alive and unmoved."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    wp, wb = _workspace(workspace)
+    full = (o, *args, int(partition_size), wp, wb, _stream(stream))
+    fn = load_library().pa_decode_v2
+
+    def call():
+        st = fn(*full)
+        if st != PA_OK:
+            raise PagedAttentionError(st, "pa_decode_v2")
+    return call
+
+
 def pa_decode_v2_single(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
                         max_seq_len, partition_size, workspace, stream=None):
     """V2 in one launch (the workspace header must be zero before the first call;
@@ -346,6 +372,31 @@ def pa_decode_v2_reduce(out, seq_lens, max_seq_len, partition_size, workspace, s
     _check(load_library().pa_decode_v2_reduce(o, sl, S, Hq, D, int(max_seq_len),
                                               _DTYPE_CODE[out.dtype], int(partition_size), wp, wb,
                                               _stream(stream)), "pa_decode_v2_reduce")
+
+
+def pa_decode_v2_groups(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
+                        partition_size, workspace, stream=None) -> int:
+    """V2 Phase 1 as pa_decode_v2 runs it; returns the partitions behind each entry."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    wp, wb = _workspace(workspace)
+    n = ctypes.c_int(0)
+    _check(load_library().pa_decode_v2_groups(*args, int(partition_size), wp, wb, ctypes.byref(n),
+                                              _stream(stream)), "pa_decode_v2_groups")
+    return int(n.value)
+
+
+def pa_decode_v2_reduce_entries(out, seq_lens, max_seq_len, partition_size, partitions_per_entry,
+                                workspace, stream=None):
+    """V2 Phase 2 over entries of partitions_per_entry partitions each."""
+    S, Hq, D = out.shape
+    o = _dev("out", out)
+    if out.dtype not in _DTYPE_CODE:
+        raise TypeError("out must be float32 or bfloat16")
+    sl = _dev("seq_lens", seq_lens, torch.int32, 1)
+    wp, wb = _workspace(workspace)
+    _check(load_library().pa_decode_v2_reduce_entries(
+        o, sl, S, Hq, D, int(max_seq_len), _DTYPE_CODE[out.dtype], int(partition_size),
+        int(partitions_per_entry), wp, wb, _stream(stream)), "pa_decode_v2_reduce_entries")
 
 
 def new_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, device="cuda"):

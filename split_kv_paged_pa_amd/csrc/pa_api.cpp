@@ -317,6 +317,7 @@ pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
         tiles = auto_tiles(true, tiles == kAutoPrefill, num_seqs, num_kv_heads,
                            num_q_heads / num_kv_heads, q_len, dtype, 1);
     if (!out) return PA_ERR_NULL_POINTER;
+    if (!aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
                                   max_blocks_per_seq, max_seq_len, scale, dtype);
@@ -325,10 +326,17 @@ pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
     return from_hip(pa::launch_single_pass(pb, out, hs));
 }
 
-// V2 Phase 1 (+ Phase 2 when out != nullptr).  With q_len query tokens per
-// sequence the partials have q_len * num_q_heads rows per sequence.  tiles > 0:
-// Phase 1 on the prefill kernel with that many column tiles per wave.
-pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *key_cache,
+// What decode_v2 runs: both phases; Phase 1 alone with one workspace entry per
+// partition; or Phase 1 alone as the two-phase form runs it (entries of
+// per_group partitions when workgroups take several), reporting the partitions
+// per entry.
+enum class V2Run { kBoth, kPartitions, kEntries };
+
+// V2 Phase 1 (+ Phase 2 for kBoth).  With q_len query tokens per sequence the
+// partials have q_len * num_q_heads rows per sequence.  tiles > 0: Phase 1 on
+// the prefill kernel with that many column tiles per wave.
+pa_status_t decode_v2(void *out, V2Run run, int *entry_parts_out, const void *query,
+                      const void *key_cache,
                       const void *value_cache, const int32_t *block_tables,
                       const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
@@ -350,11 +358,19 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
     pa::Partials parts;
     st = carve(num_seqs, (int)rows_per_seq, num_kv_heads * chunks, head_dim, max_seq_len,
                partition_size, workspace, workspace_bytes, &parts);
-    if (st != PA_OK || num_seqs == 0) return st;
-    if (want_out && !out) return PA_ERR_NULL_POINTER;
+    if (st != PA_OK) return st;
     if (tiles < 0)
         tiles = auto_tiles(false, tiles == kAutoPrefill, num_seqs, num_kv_heads,
                            num_q_heads / num_kv_heads, q_len, dtype, parts.max_parts);
+    // Workgroups with several partitions fold them into one entry (not on the
+    // prefill kernel, and not when the per-partition partials were asked for).
+    const bool grouped = run != V2Run::kPartitions && tiles <= 0 && parts.per_group > 1 &&
+                         parts.per_group <= pa::grouped_max_parts();
+    if (entry_parts_out) *entry_parts_out = grouped ? parts.per_group : 1;
+    if (num_seqs == 0) return PA_OK;
+    const bool want_out = run == V2Run::kBoth;
+    if (want_out && !out) return PA_ERR_NULL_POINTER;
+    if (want_out && !aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   q_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -362,7 +378,7 @@ pa_status_t decode_v2(void *out, bool want_out, const void *query, const void *k
     if (parts.max_parts > 0) {
         if (tiles > 0) {
             st = from_hip(pa::launch_prefill(pb, &parts, nullptr, tiles, hs));
-        } else if (want_out && parts.per_group > 1 && parts.per_group <= pa::grouped_max_parts()) {
+        } else if (grouped) {
             // Workgroups with several partitions fold them and write one group
             // partial each; Phase 2 merges those.
             st = from_hip(pa::launch_grouped(pb, parts, hs));
@@ -409,19 +425,35 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                   int max_blocks_per_seq, int max_seq_len, float scale,
                                   pa_dtype_t dtype, int partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream) {
-    return decode_v2(nullptr, false, query, key_cache, value_cache, block_tables, seq_lens,
+    return decode_v2(nullptr, V2Run::kPartitions, nullptr, query, key_cache, value_cache,
+                     block_tables, seq_lens,
                      num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
                      workspace_bytes, 0, stream);
 }
 
-pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
-                                int head_dim, int max_seq_len, pa_dtype_t dtype,
-                                int partition_size, const void *workspace, size_t workspace_bytes,
-                                void *stream) {
+pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_seq_len, float scale,
+                                pa_dtype_t dtype, int partition_size, void *workspace,
+                                size_t workspace_bytes, int *partitions_per_entry, void *stream) {
+    return decode_v2(nullptr, V2Run::kEntries, partitions_per_entry, query, key_cache, value_cache,
+                     block_tables, seq_lens, num_seqs, 1, num_q_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                     partition_size, workspace, workspace_bytes, 0, stream);
+}
+
+pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int num_seqs,
+                                        int num_q_heads, int head_dim, int max_seq_len,
+                                        pa_dtype_t dtype, int partition_size,
+                                        int partitions_per_entry, const void *workspace,
+                                        size_t workspace_bytes, void *stream) {
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
         return PA_ERR_INVALID_SHAPE;
     if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARGUMENT;
+    if (partitions_per_entry < 1) return PA_ERR_INVALID_ARGUMENT;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
     pa::Partials parts;
@@ -429,9 +461,20 @@ pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs
                            const_cast<void *>(workspace), workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (!out || !seq_lens) return PA_ERR_NULL_POINTER;
+    if (!aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
+    parts.entry_parts = partitions_per_entry;
     return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
                                       dtype == PA_DTYPE_BF16 ? pa::Dtype::BF16 : pa::Dtype::F32,
                                       parts, out, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                int head_dim, int max_seq_len, pa_dtype_t dtype,
+                                int partition_size, const void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    return pa_decode_v2_reduce_entries(out, seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
+                                       dtype, partition_size, 1, workspace, workspace_bytes,
+                                       stream);
 }
 
 pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
@@ -440,7 +483,8 @@ pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                          int max_seq_len, float scale, pa_dtype_t dtype, int partition_size,
                          void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+    return decode_v2(out, V2Run::kBoth, nullptr, query, key_cache, value_cache, block_tables,
+                     seq_lens, num_seqs,
                      1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
                      workspace_bytes, 0, stream);
@@ -453,7 +497,8 @@ pa_status_t pa_decode_v2_q(void *out, const void *query, const void *key_cache,
                            int max_blocks_per_seq, int max_seq_len, float scale,
                            pa_dtype_t dtype, int partition_size, void *workspace,
                            size_t workspace_bytes, void *stream) {
-    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+    return decode_v2(out, V2Run::kBoth, nullptr, query, key_cache, value_cache, block_tables,
+                     seq_lens, num_seqs,
                      q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
                      workspace_bytes, kAuto, stream);
@@ -477,6 +522,7 @@ pa_status_t pa_decode_v2_single(void *out, const void *query, const void *key_ca
                workspace, workspace_bytes, &parts);
     if (st != PA_OK || num_seqs == 0) return st;
     if (!out) return PA_ERR_NULL_POINTER;
+    if (!aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     pa::Problem pb = make_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                                   1, num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -510,7 +556,8 @@ pa_status_t pa_prefill_v2(void *out, const void *query, const void *key_cache,
                           int column_tiles, void *stream) {
     if (column_tiles == 0) column_tiles = kAutoPrefill;
     else if (column_tiles < 0) return PA_ERR_INVALID_ARGUMENT;
-    return decode_v2(out, true, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+    return decode_v2(out, V2Run::kBoth, nullptr, query, key_cache, value_cache, block_tables,
+                     seq_lens, num_seqs,
                      q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, workspace,
                      workspace_bytes, column_tiles, stream);

@@ -38,6 +38,24 @@ def test_phase1_bytes_by_hand():
     assert b.phase1_bytes(spec, 1024) == (kv + rest + 98 * 32 * 130 * 4, kv)
     assert b.phase1_bytes(spec, 512) == (kv + rest + 196 * 32 * 130 * 4, kv)
     assert kv == spec.kv_bytes == 204_800_000
+    # Entries of 2 (P = 1024) or 4 (P = 512) partitions: 49 entries per row.
+    assert b.phase1_bytes(spec, 1024, 2) == (kv + rest + 49 * 32 * 130 * 4, kv)
+    assert b.phase1_bytes(spec, 512, 4) == (kv + rest + 49 * 32 * 130 * 4, kv)
+
+
+def test_step_stats():
+    b = _bench()
+    st = b.step_stats([float(x) for x in range(1, 101)])
+    assert st["median"] == 50.5 and st["n"] == 100
+    assert abs(st["p10"] - 10.9) < 1e-9 and abs(st["p90"] - 90.1) < 1e-9
+
+
+def test_bench_starts_no_child_process():
+    """bench.py reads clock levels from sysfs files; it must not start a program from
+    the GPU process (under a profiler that is an exec of a preloaded process)."""
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    for word in ("subprocess", "os.system", "popen", "os.exec"):
+        assert word not in src.lower(), word
 
 
 def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
