@@ -345,6 +345,32 @@ pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
                                 pa_dtype_t dtype, int partition_size, void *workspace,
                                 size_t workspace_bytes, int *partitions_per_entry, void *stream);
 
+/*
+ * pa_decode_v2 for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments as
+ * pa_decode_v2 without the workspace, same results bit for bit.  The workspace
+ * is a file-scope device array of PA_NOALLOC_SCRATCH_BYTES in the library (one
+ * per device, held until the process ends; its device address is looked up
+ * once per device, on the first call with that device current).  The call
+ * allocates nothing -- no hipMalloc, no hipFree, no allocating library
+ * routine -- and needs nothing in the array cleared: Phase 1 writes every
+ * entry Phase 2 reads.  Returns PA_ERR_WORKSPACE_TOO_SMALL, having launched
+ * nothing, when pa_workspace_size for the problem (with the partition size in
+ * use; partition_size = 0 as in pa_decode_v2) exceeds PA_NOALLOC_SCRATCH_BYTES,
+ * and PA_ERR_HIP if the array's address cannot be obtained.  Every call on one
+ * device shares that device's array: calls that may overlap on one device (two
+ * streams, or two host threads) race and must be ordered by the caller; calls
+ * in order on one stream are safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+pa_status_t pa_decode_v2_noalloc(void *out, const void *query, const void *key_cache,
+                                 const void *value_cache, const int32_t *block_tables,
+                                 const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 int max_blocks_per_seq, int max_seq_len, float scale,
+                                 pa_dtype_t dtype, int partition_size, void *stream);
+
 /* V2 Phase 2 over entries that stand for partitions_per_entry (>= 1)
  * consecutive partitions each, as pa_decode_v2_groups writes them: reads the
  * ceil(ceil(L / partition_size) / partitions_per_entry) entries of each row.

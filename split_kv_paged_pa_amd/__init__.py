@@ -6,7 +6,7 @@ the same function names; `workloads` draws seeded synthetic decode batches.
 """
 from .api import (PagedAttentionError, bind_decode_v2, load_library, new_workspace, pa_decode, pa_decode_auto,
                   pa_decode_v1, pa_decode_v1_q, pa_decode_v2, pa_decode_v2_partials,
-                  pa_decode_v2_groups, pa_decode_v2_q, pa_decode_v2_reduce,
+                  pa_decode_v2_groups, pa_decode_v2_noalloc, pa_decode_v2_q, pa_decode_v2_reduce,
                   pa_decode_v2_reduce_entries,
                   pa_decode_v2_single, pa_prefill_v1, pa_prefill_v2, pa_select_partition_size,
                   pa_select_q_kernel, pa_select_v2, pa_select_v2_auto, pa_status_string,
@@ -14,7 +14,7 @@ from .api import (PagedAttentionError, bind_decode_v2, load_library, new_workspa
 
 __all__ = ["PagedAttentionError", "bind_decode_v2", "load_library", "new_workspace", "pa_decode", "pa_decode_auto",
            "pa_decode_v1", "pa_decode_v1_q", "pa_decode_v2", "pa_decode_v2_partials",
-           "pa_decode_v2_groups", "pa_decode_v2_q", "pa_decode_v2_reduce",
+           "pa_decode_v2_groups", "pa_decode_v2_noalloc", "pa_decode_v2_q", "pa_decode_v2_reduce",
            "pa_decode_v2_reduce_entries",
            "pa_decode_v2_single", "pa_prefill_v1", "pa_prefill_v2", "pa_select_partition_size",
            "pa_select_q_kernel", "pa_select_v2", "pa_select_v2_auto", "pa_status_string",

@@ -7,7 +7,7 @@ call raises.
 
 Functions keep the C names: pa_decode_v1, pa_decode_v2, pa_decode,
 pa_decode_v2_partials, pa_decode_v2_reduce, pa_decode_v2_groups,
-pa_decode_v2_reduce_entries, pa_workspace_size,
+pa_decode_v2_reduce_entries, pa_decode_v2_noalloc, pa_workspace_size,
 pa_workspace_layout, pa_workspace_init, pa_select_partition_size, pa_select_v2, pa_select_v2_auto,
 pa_decode_auto, pa_decode_v2_single, pa_decode_v1_q, pa_decode_v2_q, pa_prefill_v1,
 pa_prefill_v2, pa_select_q_kernel, pa_status_string.
@@ -87,6 +87,8 @@ def load_library():
     lib.pa_decode_v2_partials.restype = I
     lib.pa_decode_v2_reduce.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
     lib.pa_decode_v2_reduce.restype = I
+    lib.pa_decode_v2_noalloc.argtypes = [P] + common + [I, P]
+    lib.pa_decode_v2_noalloc.restype = I
     lib.pa_decode_v2_groups.argtypes = common + [I, P, Z, ctypes.POINTER(I), P]
     lib.pa_decode_v2_groups.restype = I
     lib.pa_decode_v2_reduce_entries.argtypes = [P, P, I, I, I, I, I, I, I, P, Z, P]
@@ -230,6 +232,21 @@ def pa_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, sca
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode_v2(o, *args, int(partition_size), wp, wb, _stream(stream)),
            "pa_decode_v2")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def pa_decode_v2_noalloc(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
+                         max_seq_len, partition_size, stream=None):
+    """pa_decode_v2 with its workspace in the library's per-device scratch array (no
+    allocation; problems whose workspace exceeds NOALLOC_SCRATCH_BYTES are refused)."""
+    args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
+    o = _dev("out", out, query.dtype)
+    if out.shape != query.shape:
+        raise ValueError("out must have the query's shape")
+    _check(load_library().pa_decode_v2_noalloc(o, *args, int(partition_size), _stream(stream)),
+           "pa_decode_v2_noalloc")
 
 
 def bind_decode_v2(out, query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,

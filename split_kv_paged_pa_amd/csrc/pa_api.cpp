@@ -2,11 +2,12 @@
 // host-side argument checks, workspace carving, V1/V2 dispatch, launches.
 // Every check happens before anything is enqueued; nothing here allocates,
 // synchronises or reads device memory.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/pa_decode.h"
 #include "pa_launch.h"
@@ -619,6 +620,73 @@ pa_status_t pa_decode(void *out, const void *query, const void *key_cache, const
     return pa_decode_v1(out, query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                         max_blocks_per_seq, max_seq_len, scale, dtype, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free V2.  The workspace of pa_decode_v2_noalloc lives in this
+// file-scope device array: each device the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, resolved once per device with that
+// device current, and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (nullptr if it cannot be had).
+void *device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();  // leave no sticky error for the caller's next call
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_v2_noalloc(void *out, const void *query, const void *key_cache,
+                                 const void *value_cache, const int32_t *block_tables,
+                                 const int32_t *seq_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 int max_blocks_per_seq, int max_seq_len, float scale,
+                                 pa_dtype_t dtype, int partition_size, void *stream) {
+    // Argument checks first, with no workspace yet: every problem error is reported
+    // as pa_decode_v2 would report it, before the size check below.
+    pa_status_t st = check_problem(query, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                                   1, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_seq_len, scale, dtype);
+    if (st != PA_OK) return st;
+    if (partition_size == 0)
+        partition_size = pa_select_partition_size(num_seqs, num_kv_heads, max_seq_len);
+    Layout lay;
+    if (partition_size < kBlockTokens || partition_size % kBlockTokens != 0)
+        return PA_ERR_UNSUPPORTED;
+    if (!layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &lay))
+        return PA_ERR_INVALID_SHAPE;
+    if (lay.total > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (num_seqs == 0) return PA_OK;
+    void *ws = device_scratch();
+    if (!ws) return PA_ERR_HIP;
+    return decode_v2(out, V2Run::kBoth, nullptr, query, key_cache, value_cache, block_tables,
+                     seq_lens, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype, partition_size, ws,
+                     PA_NOALLOC_SCRATCH_BYTES, 0, stream);
 }
 
 }  // extern "C"

@@ -182,6 +182,21 @@ def test_partition_size_rule():
     assert lib.pa_decode_v2_reduce(FAKE, FAKE, 1, 32, 128, 100000, 1, 0, FAKE, need, None) == UNSUP
 
 
+def test_noalloc_rejects_before_any_hip_call():
+    """The allocation-free entry refuses problems whose workspace exceeds its scratch
+    array (and every invalid argument) before touching the device."""
+    lib = pa.load_library()
+    # (out, query, key, value, block_tables, seq_lens, S, Hq, Hkv, D, block_size,
+    #  num_blocks, max_blocks, max_seq_len, scale, dtype, P, stream)
+    big = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 8, 128, 16, 100, 128, 2048, 0.088, 1)
+    assert pa.pa_workspace_size(64, 64, 128, 2048, 16) > pa.api.NOALLOC_SCRATCH_BYTES
+    assert lib.pa_decode_v2_noalloc(*big, 16, None) == WS
+    assert lib.pa_decode_v2_noalloc(*big[:7], 9, *big[8:], 16, None) == SHAPE   # Hq % Hkv
+    assert lib.pa_decode_v2_noalloc(*big, 24, None) == UNSUP                    # P % 16
+    assert lib.pa_decode_v2_noalloc(*big[:14], float("nan"), 1, 16, None) == ARG
+    assert lib.pa_decode_v2_noalloc(FAKE, None, *big[2:], 16, None) == NULLP
+
+
 def test_select_v2_auto_rule():
     # Above 8192 tokens: V2, as the pages' rule; at or below 1024: V1, whatever the batch.
     assert pa.pa_select_v2_auto(8193, 256, 8, 1024) is True
