@@ -87,7 +87,11 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes and dtypes are 32-bit integers with named values (not C enum
+ * types), so that a caller passing any int -- a bad dtype included -- hands the
+ * library a well-defined value to reject. */
+typedef int32_t pa_status_t;
+enum {
     PA_OK = 0,
     PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
     PA_ERR_INVALID_SHAPE = 2,      /* negative or inconsistent sizes */
@@ -96,9 +100,10 @@ typedef enum {
     PA_ERR_HIP = 5,                /* a HIP launch failed */
     PA_ERR_INVALID_ARGUMENT = 6    /* non-finite scale, bad dtype, misaligned pointer,
                                       column_tiles not 0, 1, 2 or 4 */
-} pa_status_t;
+};
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+typedef int32_t pa_dtype_t;
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *pa_status_string(pa_status_t status);

@@ -164,11 +164,12 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (lay.total > 0 && !workspace) return PA_ERR_NULL_POINTER;
     if (lay.total > 0 && !aligned16(workspace)) return PA_ERR_INVALID_ARGUMENT;
+    // A problem with nothing to hold may come with a NULL workspace: carve only a real one.
     char *base = static_cast<char *>(workspace);
     parts->tickets = reinterpret_cast<uint32_t *>(base);
-    parts->tmp_out = reinterpret_cast<float *>(base + lay.tmp_off);
-    parts->exp_sums = reinterpret_cast<float *>(base + lay.exp_off);
-    parts->max_logits = reinterpret_cast<float *>(base + lay.max_off);
+    parts->tmp_out = base ? reinterpret_cast<float *>(base + lay.tmp_off) : nullptr;
+    parts->exp_sums = base ? reinterpret_cast<float *>(base + lay.exp_off) : nullptr;
+    parts->max_logits = base ? reinterpret_cast<float *>(base + lay.max_off) : nullptr;
     parts->partition_size = partition_size;
     parts->max_parts = lay.max_parts;
     parts->per_group = partitions_per_group((long long)num_seqs * num_kv_heads * lay.max_parts);
