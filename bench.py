@@ -72,15 +72,14 @@ def kernel_sha():
     return hashlib.sha256("".join(src.split()).encode()).hexdigest()[:16]
 
 
-def phase1_bytes(spec, P, per_entry=1):
+def phase1_bytes(spec, P, entry_tokens=None):
     """Algorithmic bytes of one Phase-1 launch: each K/V row of the actual tokens
     read once (Hkv*D*es*2 per token), the query, the block-table entries used,
     seq_lens, and the workspace entries written (D+2 floats per (seq, head,
-    entry); an entry stands for per_entry consecutive partitions)."""
+    entry); an entry covers entry_tokens tokens, by default one partition)."""
     es = spec.elem_size
     lens = spec.seq_lens.astype(np.int64)
-    parts = -(-lens // P)
-    entries = int(np.sum(-(-parts // per_entry)))
+    entries = int(np.sum(-(-lens // (entry_tokens or P))))
     kv = int(lens.sum()) * spec.num_kv_heads * spec.head_dim * es * 2
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * es
     tables = int(np.sum(-(-lens // 16))) * 4 + spec.num_seqs * 4
@@ -415,12 +414,12 @@ def main():
     # around n1 back-to-back launches gives the mean duration; one pair per launch
     # gives the spread.
     wsh = workspace(args.partition_size)
-    per_entry = 1
+    entry_tokens = P
 
     def phase1(i):
-        nonlocal per_entry
+        nonlocal entry_tokens
         c = i % len(kcs)
-        per_entry = pa.pa_decode_v2_groups(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, wsh)
+        entry_tokens = pa.pa_decode_v2_groups(q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, wsh)
     n1 = max(20, min(args.steps, 100))
     for i in range(5):
         phase1(i)
@@ -433,10 +432,10 @@ def main():
     torch.cuda.synchronize()
     p1_us = e0.elapsed_time(e1) * 1e3 / n1
     durs = time_per_step(phase1, n1, stream)  # includes per-pair event overhead
-    alg_bytes, kv_bytes = phase1_bytes(spec, P, per_entry)
+    alg_bytes, kv_bytes = phase1_bytes(spec, P, entry_tokens)
     achieved = alg_bytes / (p1_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, P)
-    mode = "kPartials" if per_entry == 1 else f"kGrouped, {per_entry} partitions per workgroup"
+    mode = "kPartials" if entry_tokens == P else f"kGrouped, spans of {entry_tokens} tokens"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],

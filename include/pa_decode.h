@@ -190,13 +190,10 @@ int pa_select_partition_size(int num_seqs, int num_kv_heads, int max_seq_len);
  * head_dim, max_seq_len, partition_size) and the workspace 16-byte aligned; it
  * may be reused by later calls on the same stream, but two calls in flight at
  * once must not share it.  A sequence with L == 0 gets an all-zero output row.
- * When the partitions are few enough that one Phase-1 workgroup takes several
- * consecutive partitions (up to 4), it merges them -- each partition computed
- * and merged across its waves as in Phase 1, then folded in order with the
- * Phase-2 rescale -- and the workspace entry that Phase 2 reads holds that
- * group: after pa_decode_v2 the workspace therefore holds Phase-2 entries, not
- * necessarily one per partition (pa_decode_v2_partials writes one per
- * partition).
+ * When partitions are few, Phase 1 runs in equal spans of blocks, about one
+ * per compute unit (see pa_decode_v2_groups): after pa_decode_v2 the workspace
+ * holds Phase-2 entries, one per span, not necessarily one per partition
+ * (pa_decode_v2_partials writes one per partition).
  */
 pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,
                          const void *value_cache, const int32_t *block_tables,
@@ -332,23 +329,39 @@ pa_status_t pa_decode_v2_partials(const void *query, const void *key_cache,
                                   pa_dtype_t dtype, int partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
-/* V2 Phase 1 alone, exactly as pa_decode_v2 runs it: one workspace entry per
- * partition, or, when workgroups take several consecutive partitions, one
- * entry per such group (each partition computed and merged across the waves as
- * in Phase 1, the group's partitions then folded in order with the Phase-2
- * rescale; same layout and meaning as a partition's entry, over the group's
- * tokens).  *partitions_per_entry (may be NULL) receives the number of
- * partitions behind each entry (1, or 2 to 4), which
- * pa_decode_v2_reduce_entries takes.  Same arguments as pa_decode_v2, without
- * out; partition_size = 0 as there.  pa_decode_v2 is this call followed by
- * pa_decode_v2_reduce_entries, bit for bit. */
+/* V2 Phase 1 alone, exactly as pa_decode_v2 runs it, and the tokens behind each
+ * workspace entry it writes (*entry_tokens, may be NULL).  When partitions are
+ * many, that is one entry per partition (entry_tokens = partition_size).  When
+ * they are few (fewer than four per compute unit over all sequences and kv
+ * heads), Phase 1 splits each (sequence, kv head) into equal spans of blocks,
+ * about one span per compute unit, cutting the partitions wherever the spans
+ * fall: a workgroup computes each partition piece in its span (merged across its
+ * waves as in Phase 1), folds the pieces in order with the Phase-2 rescale, and
+ * writes one entry per span -- the same layout and meaning as a partition's
+ * entry, over the span's tokens (entry_tokens = the span, a multiple of 16, so
+ * entry e of a row covers tokens [e * entry_tokens, (e + 1) * entry_tokens)).
+ * Same arguments as pa_decode_v2, without out; partition_size = 0 as there.
+ * pa_decode_v2 is this call followed by pa_decode_v2_reduce_entries, bit for
+ * bit. */
 pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
                                 const void *value_cache, const int32_t *block_tables,
                                 const int32_t *seq_lens, int num_seqs, int num_q_heads,
                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_seq_len, float scale,
                                 pa_dtype_t dtype, int partition_size, void *workspace,
-                                size_t workspace_bytes, int *partitions_per_entry, void *stream);
+                                size_t workspace_bytes, int *entry_tokens, void *stream);
+
+/* V2 Phase 2 over workspace entries of entry_tokens tokens each (>= 1; else
+ * PA_ERR_INVALID_ARGUMENT), as pa_decode_v2_groups writes them: reads the
+ * ceil(L / entry_tokens) entries of each row.  partition_size gives the
+ * workspace layout (pa_workspace_size); the entries of a row must fit it,
+ * ceil(max_seq_len / entry_tokens) <= ceil(max_seq_len / partition_size), else
+ * PA_ERR_INVALID_SHAPE. */
+pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int num_seqs,
+                                        int num_q_heads, int head_dim, int max_seq_len,
+                                        pa_dtype_t dtype, int partition_size, int entry_tokens,
+                                        const void *workspace, size_t workspace_bytes,
+                                        void *stream);
 
 /*
  * pa_decode_v2 for callers that cannot allocate: code under HIP graph capture,
@@ -375,16 +388,6 @@ pa_status_t pa_decode_v2_noalloc(void *out, const void *query, const void *key_c
                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                  int max_blocks_per_seq, int max_seq_len, float scale,
                                  pa_dtype_t dtype, int partition_size, void *stream);
-
-/* V2 Phase 2 over entries that stand for partitions_per_entry (>= 1)
- * consecutive partitions each, as pa_decode_v2_groups writes them: reads the
- * ceil(ceil(L / partition_size) / partitions_per_entry) entries of each row.
- * partitions_per_entry < 1 gives PA_ERR_INVALID_ARGUMENT. */
-pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int num_seqs,
-                                        int num_q_heads, int head_dim, int max_seq_len,
-                                        pa_dtype_t dtype, int partition_size,
-                                        int partitions_per_entry, const void *workspace,
-                                        size_t workspace_bytes, void *stream);
 
 /* V2 Phase 2 alone: merges the workspace partials into out with the
  * log-sum-exp rescale (commit 15ef28e, "[OPT] PagedAttention V2

@@ -393,7 +393,7 @@ def pa_decode_v2_reduce(out, seq_lens, max_seq_len, partition_size, workspace, s
 
 def pa_decode_v2_groups(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len,
                         partition_size, workspace, stream=None) -> int:
-    """V2 Phase 1 as pa_decode_v2 runs it; returns the partitions behind each entry."""
+    """V2 Phase 1 as pa_decode_v2 runs it; returns the tokens behind each workspace entry."""
     args = _problem(query, key_cache, value_cache, block_tables, seq_lens, scale, max_seq_len)
     wp, wb = _workspace(workspace)
     n = ctypes.c_int(0)
@@ -402,9 +402,9 @@ def pa_decode_v2_groups(query, key_cache, value_cache, block_tables, seq_lens, s
     return int(n.value)
 
 
-def pa_decode_v2_reduce_entries(out, seq_lens, max_seq_len, partition_size, partitions_per_entry,
+def pa_decode_v2_reduce_entries(out, seq_lens, max_seq_len, partition_size, entry_tokens,
                                 workspace, stream=None):
-    """V2 Phase 2 over entries of partitions_per_entry partitions each."""
+    """V2 Phase 2 over workspace entries of entry_tokens tokens each."""
     S, Hq, D = out.shape
     o = _dev("out", out)
     if out.dtype not in _DTYPE_CODE:
@@ -413,7 +413,7 @@ def pa_decode_v2_reduce_entries(out, seq_lens, max_seq_len, partition_size, part
     wp, wb = _workspace(workspace)
     _check(load_library().pa_decode_v2_reduce_entries(
         o, sl, S, Hq, D, int(max_seq_len), _DTYPE_CODE[out.dtype], int(partition_size),
-        int(partitions_per_entry), wp, wb, _stream(stream)), "pa_decode_v2_reduce_entries")
+        int(entry_tokens), wp, wb, _stream(stream)), "pa_decode_v2_reduce_entries")
 
 
 def new_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, device="cuda"):

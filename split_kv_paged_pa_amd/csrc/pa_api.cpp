@@ -4,6 +4,7 @@
 // synchronises or reads device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -173,11 +174,44 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     parts->partition_size = partition_size;
     parts->max_parts = lay.max_parts;
     parts->per_group = partitions_per_group((long long)num_seqs * num_kv_heads * lay.max_parts);
-    parts->entry_parts = 1;
+    parts->span_blocks = 0;
+    parts->span_count = 0;
+    parts->entry_tokens = partition_size;
     return PA_OK;
 }
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Phase-1 spans for the grouped form (few work units: parts.per_group > 1).  Each
+// of the ny (kv head, column chunk) rows of a sequence is split into W equal
+// spans of blocks, W = CUs / (num_seqs * ny) -- one workgroup per compute unit --
+// but at most max_parts (the entries a workspace row holds); the spans cut the
+// partitions wherever they fall.  Measured on MI355X, one 100K-token sequence
+// with 4 kv heads: 64 spans of 98 blocks per kv head (256 workgroups) against
+// 196 workgroups of two whole 1024-token partitions, the step 40.42 -> 40.12 us
+// at P 1024 and 40.92 -> 40.68 us at P 512 (per-step medians, one box).  Falls
+// back to whole
+// partitions (per_group per workgroup, at most kGroupFewUnits <= the slots of a
+// 16-column workgroup) when a span could cut more partitions than a workgroup
+// has piece slots for.
+void grouped_spans(int num_seqs, int ny, int max_seq_len, int columns, pa::Partials *parts) {
+    const int bp = parts->partition_size / kBlockTokens;
+    const long long nblk = ((long long)max_seq_len + kBlockTokens - 1) / kBlockTokens;
+    const int cus = compute_units();
+    long long w = cus > 0 ? cus / ((long long)num_seqs * ny) : 0;
+    if (w > parts->max_parts) w = parts->max_parts;
+    if (w >= 1 && nblk > 0) {
+        const long long span = (nblk + w - 1) / w;
+        if (pa::grouped_span_pieces(span, bp) <= pa::grouped_max_pieces(columns) &&
+            span <= 0x7fffffffLL) {
+            parts->span_blocks = (int)span;
+            parts->span_count = (int)((nblk + span - 1) / span);
+            return;
+        }
+    }
+    parts->span_blocks = parts->per_group * bp;  // whole partitions, aligned
+    parts->span_count = (parts->max_parts + parts->per_group - 1) / parts->per_group;
+}
 
 // Kernel selection of decode_v1 / decode_v2 (their tiles argument):
 //   0          the decode kernel;
@@ -329,15 +363,14 @@ pa_status_t decode_v1(void *out, const void *query, const void *key_cache,
 }
 
 // What decode_v2 runs: both phases; Phase 1 alone with one workspace entry per
-// partition; or Phase 1 alone as the two-phase form runs it (entries of
-// per_group partitions when workgroups take several), reporting the partitions
-// per entry.
+// partition; or Phase 1 alone as the two-phase form runs it (entries of equal
+// block spans when partitions are few), reporting the tokens per entry.
 enum class V2Run { kBoth, kPartitions, kEntries };
 
 // V2 Phase 1 (+ Phase 2 for kBoth).  With q_len query tokens per sequence the
 // partials have q_len * num_q_heads rows per sequence.  tiles > 0: Phase 1 on
 // the prefill kernel with that many column tiles per wave.
-pa_status_t decode_v2(void *out, V2Run run, int *entry_parts_out, const void *query,
+pa_status_t decode_v2(void *out, V2Run run, int *entry_tokens_out, const void *query,
                       const void *key_cache,
                       const void *value_cache, const int32_t *block_tables,
                       const int32_t *seq_lens, int num_seqs, int q_len, int num_q_heads,
@@ -364,11 +397,15 @@ pa_status_t decode_v2(void *out, V2Run run, int *entry_parts_out, const void *qu
     if (tiles < 0)
         tiles = auto_tiles(false, tiles == kAutoPrefill, num_seqs, num_kv_heads,
                            num_q_heads / num_kv_heads, q_len, dtype, parts.max_parts);
-    // Workgroups with several partitions fold them into one entry (not on the
+    // Few partitions: Phase 1 in equal spans, one entry per span (not on the
     // prefill kernel, and not when the per-partition partials were asked for).
-    const bool grouped = run != V2Run::kPartitions && tiles <= 0 && parts.per_group > 1 &&
-                         parts.per_group <= pa::grouped_max_parts();
-    if (entry_parts_out) *entry_parts_out = grouped ? parts.per_group : 1;
+    const bool grouped = run != V2Run::kPartitions && tiles <= 0 && parts.per_group > 1;
+    if (grouped) {
+        const int columns = (int)std::min<long long>(16, (long long)(num_q_heads / num_kv_heads) * q_len);
+        grouped_spans(num_seqs, num_kv_heads * chunks, max_seq_len, columns, &parts);
+    }
+    if (entry_tokens_out)
+        *entry_tokens_out = grouped ? parts.span_blocks * kBlockTokens : partition_size;
     if (num_seqs == 0) return PA_OK;
     const bool want_out = run == V2Run::kBoth;
     if (want_out && !out) return PA_ERR_NULL_POINTER;
@@ -384,7 +421,7 @@ pa_status_t decode_v2(void *out, V2Run run, int *entry_parts_out, const void *qu
             // Workgroups with several partitions fold them and write one group
             // partial each; Phase 2 merges those.
             st = from_hip(pa::launch_grouped(pb, parts, hs));
-            parts.entry_parts = parts.per_group;
+            parts.entry_tokens = parts.span_blocks * kBlockTokens;
         } else {
             st = from_hip(pa::launch_partitions(pb, parts, hs));
         }
@@ -440,8 +477,8 @@ pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_seq_len, float scale,
                                 pa_dtype_t dtype, int partition_size, void *workspace,
-                                size_t workspace_bytes, int *partitions_per_entry, void *stream) {
-    return decode_v2(nullptr, V2Run::kEntries, partitions_per_entry, query, key_cache, value_cache,
+                                size_t workspace_bytes, int *entry_tokens, void *stream) {
+    return decode_v2(nullptr, V2Run::kEntries, entry_tokens, query, key_cache, value_cache,
                      block_tables, seq_lens, num_seqs, 1, num_q_heads, num_kv_heads, head_dim,
                      block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
                      partition_size, workspace, workspace_bytes, 0, stream);
@@ -449,22 +486,26 @@ pa_status_t pa_decode_v2_groups(const void *query, const void *key_cache,
 
 pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int num_seqs,
                                         int num_q_heads, int head_dim, int max_seq_len,
-                                        pa_dtype_t dtype, int partition_size,
-                                        int partitions_per_entry, const void *workspace,
-                                        size_t workspace_bytes, void *stream) {
+                                        pa_dtype_t dtype, int partition_size, int entry_tokens,
+                                        const void *workspace, size_t workspace_bytes,
+                                        void *stream) {
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
         return PA_ERR_INVALID_SHAPE;
     if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARGUMENT;
-    if (partitions_per_entry < 1) return PA_ERR_INVALID_ARGUMENT;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
     pa::Partials parts;
     pa_status_t st = carve(num_seqs, num_q_heads, 1, head_dim, max_seq_len, partition_size,
                            const_cast<void *>(workspace), workspace_bytes, &parts);
-    if (st != PA_OK || num_seqs == 0) return st;
+    if (st != PA_OK) return st;
+    if (entry_tokens < 1) return PA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return PA_OK;
     if (!out || !seq_lens) return PA_ERR_NULL_POINTER;
     if (!aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
-    parts.entry_parts = partitions_per_entry;
+    // The entries of a row must fit the row the workspace holds.
+    if (max_seq_len > 0 && ((long long)max_seq_len + entry_tokens - 1) / entry_tokens > parts.max_parts)
+        return PA_ERR_INVALID_SHAPE;
+    parts.entry_tokens = entry_tokens;
     return from_hip(pa::launch_reduce(seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
                                       dtype == PA_DTYPE_BF16 ? pa::Dtype::BF16 : pa::Dtype::F32,
                                       parts, out, static_cast<hipStream_t>(stream)));
@@ -475,8 +516,8 @@ pa_status_t pa_decode_v2_reduce(void *out, const int32_t *seq_lens, int num_seqs
                                 int partition_size, const void *workspace, size_t workspace_bytes,
                                 void *stream) {
     return pa_decode_v2_reduce_entries(out, seq_lens, num_seqs, num_q_heads, head_dim, max_seq_len,
-                                       dtype, partition_size, 1, workspace, workspace_bytes,
-                                       stream);
+                                       dtype, partition_size, partition_size, workspace,
+                                       workspace_bytes, stream);
 }
 
 pa_status_t pa_decode_v2(void *out, const void *query, const void *key_cache,

@@ -141,9 +141,10 @@ template <> struct Mma<float> {
 };
 
 constexpr int kMergeCap = 2048;  // group partials (heads x groups) one fused merge can weigh
-// Partitions one kGrouped workgroup can hold (per-partition wave states in LDS:
-// 4 x 4 waves x 16 columns x 132 floats = 132 KiB at D = 128, of gfx950's 160 KiB).
-constexpr int kMaxGroupedParts = 4;
+// Piece slots of a kGrouped workgroup, counted at 16 columns: per-piece wave states
+// in LDS, 4 x 4 waves x 16 columns x 132 floats = 132 KiB at D = 128, of gfx950's
+// 160 KiB; stored column-compact, so 8 columns hold 8 slots.
+constexpr int kGroupedSlots16 = 4;
 
 
 // ---------------------------------------------------------------------------
@@ -267,12 +268,12 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     int num_kv_heads, int group, int qlen, int num_blocks, int max_blocks, int max_seq_len,
     float scale, int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
     float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
-    T *__restrict__ out) {
+    T *__restrict__ out, int span_blocks) {
     constexpr bool kFinal = MODE == kSinglePass;
     // kFused folds each partition into the workgroup's group partial at its close;
     // kGrouped deposits per-partition wave states (KP slots) and folds at the end.
     constexpr bool kFold = MODE == kFused;
-    constexpr int KP = MODE == kGrouped ? kMaxGroupedParts : 1;
+    constexpr int KP = MODE == kGrouped ? kGroupedSlots16 : 1;
     using M = Mma<T>;
     constexpr int E = M::E;
     using VU = typename M::VU;
@@ -280,7 +281,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     constexpr int NT = D / 16;               // d tiles: value units and accumulator tiles
     constexpr int LDS_STRIDE = D + 4;
 
-    // Per (partition slot, wave, column) states: max, exp-sum, merge factor, output.
+    // Per (piece slot, wave, column) states: max, exp-sum, merge factor, output.
+    // kGrouped indexes them column-compact, row (k * NW + w) * ncol + g, so a
+    // workgroup holds KP * 16 / ncol piece slots (8 at 8 columns).
     __shared__ float sm_m[KP][NW][16];
     __shared__ float sm_l[KP][NW][16];
     __shared__ float sm_f[KP][NW][16];
@@ -291,8 +294,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __shared__ float sm_gw[GA];
     __shared__ float sm_gs[GA];  // rescale of sm_ga for the partition being folded in
     __shared__ __attribute__((aligned(16))) float sm_ga[GA][kFold ? D : 1];
-    // kGrouped: rescale of the group partial before partition slot k is folded in,
-    // and the group's exp-sum.
+    // kGrouped: rescale of the group partial before piece slot k is folded in
+    // (index k * ncol + g), and the group's exp-sum.
     __shared__ float sm_ks[KP][16];
     __shared__ float sm_kw[MODE == kGrouped ? 16 : 1];
     __shared__ uint32_t sm_ticket;
@@ -326,21 +329,39 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     // its table entry is requested together with seq_lens[s] (index clamped into
     // the row), so the two scalar loads share one memory latency.
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
-    const int j_first = (kFinal ? 0 : pg * ppw * (partition_size / kBlockTokens)) + w;
+    const int j_first = (kFinal ? 0
+                                : MODE == kGrouped ? pg * span_blocks
+                                                   : pg * ppw * (partition_size / kBlockTokens)) + w;
     const int id_first = max_blocks > 0 ? bt[min(j_first, max_blocks - 1)] : 0;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
     // Partitions of this workgroup, in blocks of bp each.
-    int bp, p_begin, p_end;
+    // The workgroup's blocks [b_lo, b_hi) fall in partitions p_begin .. p_end - 1;
+    // piece p of them is [max(p * bp, b_lo), min((p + 1) * bp, b_hi)).  kGrouped
+    // takes span_blocks blocks from pg * span_blocks, whatever the partition
+    // boundaries (a partition cut by the span is finished by Phase 2's merge);
+    // the other modes take ppw whole partitions.
+    int bp, p_begin, p_end, b_lo, b_hi;
     if (kFinal) {
         bp = max(nblk, 1);
         p_begin = 0;
         p_end = 1;
+        b_lo = 0;
+        b_hi = nblk;
+    } else if (MODE == kGrouped) {
+        bp = partition_size / kBlockTokens;
+        b_lo = pg * span_blocks;
+        b_hi = min(b_lo + span_blocks, nblk);
+        if (b_lo >= b_hi) return;  // uniform: past the sequence's last block
+        p_begin = b_lo / bp;
+        p_end = (b_hi - 1) / bp + 1;
     } else {
         bp = partition_size / kBlockTokens;
         const int parts = (nblk + bp - 1) / bp;
         p_begin = pg * ppw;
         p_end = min(p_begin + ppw, parts);
+        b_lo = p_begin * bp;
+        b_hi = min(p_end * bp, nblk);
         if (p_begin >= p_end) {  // uniform over the workgroup
             if (MODE == kFused && parts == 0 && blockIdx.x == 0) {
                 // No workgroup of this (sequence, kv head) has work: L == 0 gives zeros.
@@ -358,7 +379,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             sm_gw[threadIdx.x] = 0.f;
         }
     }
-    auto part_end = [&](int p) { return min((p + 1) * bp, nblk); };  // end block of partition p
 
     // Columns: column g of the MFMA tiles is global column c = c0 + g, i.e. (query
     // token c / G, head kvh*G + c % G) of this sequence, for c < G * qlen (qlen query
@@ -404,18 +424,16 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     const int lim = g < ncol ? L - qlen + (c0 + g) / group : L - 1;
     const int lim_min = L - qlen + c0 / group;  // smallest limit over this chunk's columns
 
-    // ---- issue side: wave w takes blocks p*bp + w, p*bp + w + NW, ... of each of
-    // the workgroup's partitions p in turn; loads run U-1 blocks ahead of the math
-    // in a ring of register slots, across partition boundaries.  The next block
-    // id is read one issue ahead with a scalar load.
-    int i_p = p_begin;                 // partition of the next block to issue (p_end: done)
-    int i_j = p_begin * bp + w;        // next block to issue
-    auto settle = [&]() {
-        while (i_p < p_end && i_j >= part_end(i_p)) {
-            ++i_p;
-            i_j = i_p * bp + w;
-        }
-    };
+    // ---- issue side: wave w takes blocks b_lo + w, b_lo + w + NW, ... of the
+    // workgroup's whole range, so the waves' shares differ by at most one block
+    // however the partitions cut it (restarting the stride at every piece left up
+    // to one block per piece of imbalance); the piece of a block is the partition
+    // it falls in.  Loads run U-1 blocks ahead of the math in a ring of register
+    // slots, across piece boundaries.  The next block id is read one issue ahead
+    // with a scalar load.
+    int i_p = p_begin;     // piece of the next block to issue (p_end: done)
+    int i_j = b_lo + w;    // next block to issue
+    auto settle = [&]() { i_p = i_j < b_hi ? (kFinal ? 0 : i_j / bp) : p_end; };
     settle();
     int id_next = i_p < p_end ? (i_j == j_first ? id_first : bt[i_j]) : 0;
 
@@ -526,21 +544,40 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         }
     };
 
-    // End of partition p: merge the waves' states (fixed order) and write (or,
-    // kFold, fold them into the group partial).  kGrouped: deposit this wave's
-    // state in partition slot p - p_begin, without a barrier (merged at the end).
+    // kGrouped slot rows (column-compact): state row r = (k * NW + w) * ncol + g.
+    float *const fm = &sm_m[0][0][0];
+    float *const fl = &sm_l[0][0][0];
+    float *const ff = &sm_f[0][0][0];
+    float *const fo = &sm_o[0][0][0][0];
+    float *const fks = &sm_ks[0][0];
+
+    // End of piece p: merge the waves' states (fixed order) and write (or, kFold,
+    // fold them into the group partial).  kGrouped: deposit this wave's state in
+    // piece slot p - p_begin, without a barrier (merged at the end).
     auto finish = [&](int p) {
         const float l_col = column_sum(l_run);
-        const int k = MODE == kGrouped ? p - p_begin : 0;
-        if (MODE != kGrouped) __syncthreads();  // the previous partition's readers are done
-        // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of head g.
-        if (grp == 0) {
-            sm_m[k][w][g] = m_run;
-            sm_l[k][w][g] = l_col;
-        }
+        if (MODE == kGrouped) {
+            // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of head g.
+            if (g < ncol) {
+                const int r = ((p - p_begin) * NW + w) * ncol + g;
+                if (grp == 0) {
+                    fm[r] = m_run;
+                    fl[r] = l_col;
+                }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4 *>(&sm_o[k][w][g][16 * t + 4 * grp]) = acc[t];
+                for (int t = 0; t < NT; ++t)
+                    *reinterpret_cast<f32x4 *>(fo + r * LDS_STRIDE + 16 * t + 4 * grp) = acc[t];
+            }
+        } else {
+            __syncthreads();  // the previous partition's readers are done
+            if (grp == 0) {
+                sm_m[0][w][g] = m_run;
+                sm_l[0][w][g] = l_col;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4 *>(&sm_o[0][w][g][16 * t + 4 * grp]) = acc[t];
+        }
         m_run = -INFINITY;
         l_run = 0.f;
 #pragma unroll
@@ -643,33 +680,34 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         // same arithmetic as the kFused close: M' = max(M, m_p), W = W a + s_p b
         // with a = exp(M - M'), b = exp(m_p - M') -- then write it, normalised,
         // to entry blockIdx.x of the row.
-        const int np = p_end - p_begin;  // 1 .. KP, uniform
+        const int np = p_end - p_begin;  // 1 .. KP * 16 / ncol pieces, uniform
         __syncthreads();
-        if (threadIdx.x < 16) {
+        if (threadIdx.x < ncol) {
             const int gg = threadIdx.x;
             float gm = -INFINITY, gw = 0.f;
             for (int k = 0; k < np; ++k) {
+                const int r0 = k * NW * ncol + gg;  // row of wave 0; wave ww at r0 + ww * ncol
                 float mx = -INFINITY;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm_m[k][ww][gg]);
+                for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, fm[r0 + ww * ncol]);
                 float f[NW];
                 float total = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
-                    f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[k][ww][gg] - mx);
-                    total += f[ww] * sm_l[k][ww][gg];
+                    f[ww] = (mx == -INFINITY) ? 0.f : exp_e(fm[r0 + ww * ncol] - mx);
+                    total += f[ww] * fl[r0 + ww * ncol];
                 }
                 const float gm_new = fmaxf(gm, mx);
                 const float a = gm == -INFINITY ? 0.f : exp_e(gm - gm_new);
                 const float b = mx == -INFINITY ? 0.f : exp_e(mx - gm_new);
                 gw = gw * a + total * b;
                 gm = gm_new;
-                sm_ks[k][gg] = a;
+                fks[k * ncol + gg] = a;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) sm_f[k][ww][gg] = f[ww] * b;
+                for (int ww = 0; ww < NW; ++ww) ff[r0 + ww * ncol] = f[ww] * b;
             }
             sm_kw[gg] = gw;
-            if (gg < ncol) {
+            {
                 const size_t row = qrow_of(gg) * max_parts + blockIdx.x;
                 store_through(exp_sums + row, gw);
                 store_through(max_logits + row, gm);
@@ -682,11 +720,13 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
             const int d = (idx - gg * C4) * 4;
             f32x4 ga = {0.f, 0.f, 0.f, 0.f};
             for (int k = 0; k < np; ++k) {
+                const int r0 = k * NW * ncol + gg;
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww)
-                    o += sm_f[k][ww][gg] * *reinterpret_cast<const f32x4 *>(&sm_o[k][ww][gg][d]);
-                ga = ga * sm_ks[k][gg] + o;
+                    o += ff[r0 + ww * ncol] *
+                         *reinterpret_cast<const f32x4 *>(fo + (r0 + ww * ncol) * LDS_STRIDE + d);
+                ga = ga * fks[k * ncol + gg] + o;
             }
             const float W = sm_kw[gg];
             ga = ga * (W > 0.f ? 1.f / W : 0.f);
@@ -1083,7 +1123,9 @@ hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hi
     const int group = pb.num_q_heads / pb.num_kv_heads;
     const int ppw = kFinal ? 1 : parts->per_group;
     const int nchunk = (group * pb.qlen + 15) / 16;  // 16 (query token, head) columns per workgroup
-    dim3 grid(kFinal ? 1 : (parts->max_parts + ppw - 1) / ppw, pb.num_kv_heads * nchunk, pb.num_seqs);
+    const int gx = kFinal ? 1 : MODE == kGrouped ? parts->span_count
+                                                : (parts->max_parts + ppw - 1) / ppw;
+    dim3 grid(gx, pb.num_kv_heads * nchunk, pb.num_seqs);
     attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), MODE><<<grid, kWaves * 64, 0, stream>>>(
         static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
         static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
@@ -1091,7 +1133,7 @@ hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hi
         kFinal ? kBlockTokens : parts->partition_size, ppw, kFinal ? 0 : parts->max_parts,
         kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
         kFinal ? nullptr : parts->max_logits, MODE == kFused ? parts->tickets : nullptr,
-        static_cast<T *>(out));
+        static_cast<T *>(out), MODE == kGrouped ? parts->span_blocks : 0);
     return hipGetLastError();
 }
 
@@ -1109,16 +1151,13 @@ template <typename T, int D>
 hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_heads, int max_seq_len,
                            const Partials &in, void *out, hipStream_t stream) {
     const long long rows = (long long)num_seqs * num_q_heads;
-    // Entries of a row stand for entry_parts partitions each: the kernels count
-    // ceil(L / (P * entry_parts)) = ceil(ceil(L / P) / entry_parts) of them.  A
-    // span at or beyond max_seq_len is one entry per non-empty row, and is passed
-    // as max_seq_len so that it fits an int.
+    // Entries of a row stand for entry_tokens tokens each: the kernels count
+    // ceil(L / entry_tokens) of them (they take entry_tokens as their partition size).
     Partials parts = in;
-    const int ep = in.entry_parts > 1 ? in.entry_parts : 1;
-    const long long span = (long long)in.partition_size * ep;
-    if (ep > 1 && span >= max_seq_len) parts.partition_size = max_seq_len > 0 ? max_seq_len : 1;
-    else parts.partition_size = (int)span;
-    const int entries = (in.max_parts + ep - 1) / ep;  // most entries a row can hold
+    parts.partition_size = in.entry_tokens;
+    const int entries = max_seq_len > 0
+                            ? (int)(((long long)max_seq_len + in.entry_tokens - 1) / in.entry_tokens)
+                            : 0;  // most entries a row holds
     if (entries <= kRowReduceMaxParts ||
         (rows >= kRowReduceManyRows && entries <= kRowReduceManyRowsMaxParts)) {
         dim3 grid((num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, num_seqs);
@@ -1158,12 +1197,19 @@ hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream
     return dispatch_attend<kPartials>(pb, &parts, nullptr, stream);
 }
 
-hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream) {
-    if (parts.per_group < 1 || parts.per_group > kMaxGroupedParts) return hipErrorInvalidValue;
-    return dispatch_attend<kGrouped>(pb, &parts, nullptr, stream);
+int grouped_max_pieces(int columns) {
+    return columns >= 1 && columns <= 16 ? kGroupedSlots16 * 16 / columns : 0;
 }
 
-int grouped_max_parts() { return kMaxGroupedParts; }
+hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream) {
+    // Every span must touch at most grouped_max_pieces partitions (the LDS slots).
+    const int bp = parts.partition_size / kBlockTokens;
+    const int columns = min(16, pb.num_q_heads / pb.num_kv_heads * pb.qlen);
+    if (parts.span_blocks < 1 || parts.span_count < 1 ||
+        grouped_span_pieces(parts.span_blocks, bp) > grouped_max_pieces(columns))
+        return hipErrorInvalidValue;
+    return dispatch_attend<kGrouped>(pb, &parts, nullptr, stream);
+}
 
 hipError_t launch_fused(const Problem &pb, const Partials &parts, void *out, hipStream_t stream) {
     return dispatch_attend<kFused>(pb, &parts, out, stream);

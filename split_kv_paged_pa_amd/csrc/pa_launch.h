@@ -33,19 +33,30 @@ struct Partials {
     int partition_size;
     int max_parts;   // entries per row of the three arrays (the row stride)
     int per_group;   // consecutive partitions handled by one Phase-1 workgroup
-    int entry_parts; // partitions behind each entry Phase 2 reads: 1 after launch_partitions,
-                     // per_group after launch_grouped
+    int span_blocks; // launch_grouped: blocks per workgroup (any partition boundaries inside)
+    int span_count;  // launch_grouped: workgroups per (sequence, kv head, chunk)
+    int entry_tokens;  // tokens behind each entry Phase 2 reads: partition_size after
+                       // launch_partitions, 16 * span_blocks after launch_grouped
 };
 
 // V1: one workgroup per (kv head, sequence) over the whole sequence -> out.
 hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream);
 // V2 Phase 1: one workgroup per (partition, kv head, sequence) -> partials.
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream);
-// V2 Phase 1 with per_group > 1: the same grid; each workgroup folds its partitions
-// into one group partial (the Phase-2 rescale) and writes it to entry blockIdx.x
-// of the row -> Phase 2 then runs with entry_parts = per_group.
+// V2 Phase 1 as equal spans: workgroup x of a (sequence, kv head, chunk) takes
+// blocks [x * span_blocks, (x + 1) * span_blocks), computes each partition piece
+// in it, folds the pieces (the Phase-2 rescale) and writes one entry x of the
+// row -> Phase 2 then runs with entry_tokens = 16 * span_blocks.  The span may
+// cut at most grouped_max_pieces(columns) partitions (columns = min(16, G *
+// qlen)).
 hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream);
-int grouped_max_parts();  // largest per_group launch_grouped takes
+int grouped_max_pieces(int columns);
+// Most partitions (of bp blocks) that a span of span_blocks blocks starting at a
+// multiple of span_blocks can touch: span / bp when the spans are aligned to the
+// partitions, else one more than a span that starts at a boundary.
+inline long long grouped_span_pieces(long long span_blocks, int bp) {
+    return span_blocks % bp == 0 ? span_blocks / bp : (span_blocks - 1 + bp - 1) / bp + 1;
+}
 // V2 in one launch: the Phase-1 grid; each workgroup folds its partitions into a
 // group partial, and the last workgroup of each (sequence, kv head) merges them -> out.
 // Needs group * ceil(max_parts / per_group) <= fused_merge_capacity().
@@ -62,8 +73,8 @@ hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, i
                           hipStream_t stream);
 // Workgroups per kv head in grid y of launch_prefill.
 int prefill_column_groups(int group, int qlen, int nct);
-// V2 Phase 2: partials -> out.  Row r of sequence s holds ceil(ceil(L_s / P) /
-// entry_parts) valid entries (P = partition_size).
+// V2 Phase 2: partials -> out.  Row r of sequence s holds ceil(L_s / entry_tokens)
+// valid entries.
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,
                          int max_seq_len, Dtype dtype, const Partials &parts, void *out,
                          hipStream_t stream);

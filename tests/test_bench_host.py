@@ -38,9 +38,9 @@ def test_phase1_bytes_by_hand():
     assert b.phase1_bytes(spec, 1024) == (kv + rest + 98 * 32 * 130 * 4, kv)
     assert b.phase1_bytes(spec, 512) == (kv + rest + 196 * 32 * 130 * 4, kv)
     assert kv == spec.kv_bytes == 204_800_000
-    # Entries of 2 (P = 1024) or 4 (P = 512) partitions: 49 entries per row.
-    assert b.phase1_bytes(spec, 1024, 2) == (kv + rest + 49 * 32 * 130 * 4, kv)
-    assert b.phase1_bytes(spec, 512, 4) == (kv + rest + 49 * 32 * 130 * 4, kv)
+    # Entries of 1568-token spans (Phase 1 in equal spans): 64 entries per row.
+    assert b.phase1_bytes(spec, 1024, 1568) == (kv + rest + 64 * 32 * 130 * 4, kv)
+    assert b.phase1_bytes(spec, 512, 2048) == (kv + rest + 49 * 32 * 130 * 4, kv)
 
 
 def test_step_stats():

@@ -102,29 +102,29 @@ def test_grouped_partitions(name, lens, hkv, P):
 
 @pytest.mark.parametrize("name,lens,hkv,P", GROUPED, ids=[g[0] for g in GROUPED])
 def test_grouped_entries(name, lens, hkv, P):
-    """Phase 1 as pa_decode_v2 runs it (pa_decode_v2_groups): a workgroup with k
-    partitions writes one entry for their union, which is the partial of one
-    partition of P * k tokens -- compared with the oracle's partials at P * k.
-    Then Phase 2 over those entries reproduces pa_decode_v2 bit for bit."""
+    """Phase 1 as pa_decode_v2 runs it (pa_decode_v2_groups): with few partitions,
+    equal spans of entry_tokens tokens, each entry the partial of the span's tokens
+    -- compared with the oracle's partials at partition size entry_tokens.  Then
+    Phase 2 over those entries reproduces pa_decode_v2 bit for bit."""
     spec = wl.custom(name, 112, "bf16", hkv * 8, hkv, 128, lens)
     b = wl.generate(spec)
     db = DeviceBatch(b)
-    print(f"[case] grouped entries {name}", flush=True)
     ws = db.workspace(P)
-    k = pa.pa_decode_v2_groups(*db.args(), P, ws)
-    assert k > 1, "these shapes take several partitions per workgroup on 256 CUs"
+    et = pa.pa_decode_v2_groups(*db.args(), P, ws)
+    print(f"[case] grouped entries {name}: {et} tokens per entry", flush=True)
+    assert et % 16 == 0 and et != P, "these shapes take equal spans on 256 CUs"
     tmp, es, ml = (to_f64(x) for x in pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads,
                                                          spec.head_dim, db.max_seq_len, P))
     q, kc, vc, bt, sl = b.numpy()
-    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, P * k, dtype="bf16")
+    rtmp, res, rml = oracle.partials(q, kc, vc, bt, sl, spec.scale, et, dtype="bf16")
     for s_, L in enumerate(sl):
-        n = oracle.num_partitions(L, P * k)
-        assert n == -(-oracle.num_partitions(L, P) // k)
+        n = oracle.num_partitions(L, et)
+        assert n <= tmp.shape[2]
         assert np.all(np.abs(ml[s_, :, :n] - rml[s_, :, :n]) <= 1e-5 * (1 + np.abs(rml[s_, :, :n])))
         assert np.all(np.abs(es[s_, :, :n] - res[s_, :, :n]) <= 1e-2 * res[s_, :, :n])
-        assert_close(tmp[s_, :, :n], rtmp[s_, :, :n], "bf16", f"group entries s={s_}")
+        assert_close(tmp[s_, :, :n], rtmp[s_, :, :n], "bf16", f"span entries s={s_}")
     out = db.new_out()
-    pa.pa_decode_v2_reduce_entries(out, db.seq_lens, db.max_seq_len, P, k, ws)
+    pa.pa_decode_v2_reduce_entries(out, db.seq_lens, db.max_seq_len, P, et, ws)
     ref = db.run_v2(P)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
