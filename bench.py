@@ -19,7 +19,8 @@ Prints one JSON line:
     events, whichever is longer;
   - step_us: median, p10 and p90 of the same form from one event pair per step;
   - variants: the same per-step statistics for V2 at P = 512, at the library's
-    partition size (partition_size = 0), and for V1;
+    partition size (partition_size = 0), and for V1, each with the mean of the
+    same number of steps run back to back (back_to_back_mean);
   - roofline: the dominant kernel -- Phase 1 exactly as the step runs it
     (pa_decode_v2_groups) -- timed with HIP events on the launch stream, its
     algorithmic bytes, and the HBM traffic measured by rocprofv3 counters when
@@ -395,11 +396,23 @@ def main():
     step_us = step_stats(time_per_step(step, n_steps, stream))
 
     def form_line(run, n):
+        """Per-step statistics of one form (an event pair per step, so each step
+        also carries the pair's own overhead), then the mean of n steps run back
+        to back between one event pair, as the headline value is taken."""
         for i in range(5 if n > 5 else 1):
             run(i)
         st = step_stats(time_per_step(run, n, stream))
         st["gb_per_s"] = round(spec.kv_bytes / (st["median"] * 1e-6) / 1e9, 1)
         st["hbm_peak_frac"] = round(st["gb_per_s"] / HBM_PEAK_GBS, 4)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for i in range(n):
+            run(i)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        st["back_to_back_mean"] = round(b0.elapsed_time(b1) * 1e3 / n, 2)
+        st["back_to_back_gb_per_s"] = round(spec.kv_bytes / (st["back_to_back_mean"] * 1e-6) / 1e9, 1)
         return st
     variants = {}
     if not args.no_variants:
@@ -407,8 +420,8 @@ def main():
         variants["v2_auto"] = dict(form_line(forms[2][1], n_steps), partition_size=P_auto)
         variants["v1"] = form_line(v1_step, 5)
         for k, v in variants.items():
-            print(f"[bench] {k}: median {v['median']} us (p10 {v['p10']}, p90 {v['p90']})",
-                  file=sys.stderr, flush=True)
+            print(f"[bench] {k}: median {v['median']} us (p10 {v['p10']}, p90 {v['p90']}), "
+                  f"back to back {v['back_to_back_mean']} us", file=sys.stderr, flush=True)
 
     # Dominant kernel alone: V2 Phase 1 exactly as the step runs it.  An event pair
     # around n1 back-to-back launches gives the mean duration; one pair per launch
