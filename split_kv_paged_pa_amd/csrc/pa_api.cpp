@@ -177,6 +177,7 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     parts->span_blocks = 0;
     parts->span_count = 0;
     parts->entry_tokens = partition_size;
+    parts->marked_entries = -1;
     return PA_OK;
 }
 
@@ -185,32 +186,22 @@ pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP
 // Phase-1 spans for the grouped form (few work units: parts.per_group > 1).  Each
 // of the ny (kv head, column chunk) rows of a sequence is split into W equal
 // spans of blocks, W = CUs / (num_seqs * ny) -- one workgroup per compute unit --
-// but at most max_parts (the entries a workspace row holds); the spans cut the
-// partitions wherever they fall.  Measured on MI355X, one 100K-token sequence
-// with 4 kv heads: 64 spans of 98 blocks per kv head (256 workgroups) against
-// 196 workgroups of two whole 1024-token partitions, the step 40.42 -> 40.12 us
-// at P 1024 and 40.92 -> 40.68 us at P 512 (per-step medians, one box).  Falls
-// back to whole
-// partitions (per_group per workgroup, at most kGroupFewUnits <= the slots of a
-// 16-column workgroup) when a span could cut more partitions than a workgroup
-// has piece slots for.
-void grouped_spans(int num_seqs, int ny, int max_seq_len, int columns, pa::Partials *parts) {
-    const int bp = parts->partition_size / kBlockTokens;
+// but at most max_parts (the entries a workspace row holds); each span is one
+// partition of its workgroup, whatever boundaries of the caller's partition size
+// fall inside it.  Measured on MI355X, one 100K-token sequence with 4 kv heads
+// (64 spans of 98 blocks per kv head, 256 workgroups, against 196 workgroups of
+// two whole 1024-token partitions each): the step 40.42 -> 40.12 us at P 1024
+// and 40.92 -> 40.68 us at P 512 with the caller's partitions closed inside the
+// spans, 36.9 us at both once the span is one partition.
+void grouped_spans(int num_seqs, int ny, int max_seq_len, pa::Partials *parts) {
     const long long nblk = ((long long)max_seq_len + kBlockTokens - 1) / kBlockTokens;
     const int cus = compute_units();
-    long long w = cus > 0 ? cus / ((long long)num_seqs * ny) : 0;
+    long long w = cus > 0 ? cus / ((long long)num_seqs * ny) : 1;
     if (w > parts->max_parts) w = parts->max_parts;
-    if (w >= 1 && nblk > 0) {
-        const long long span = (nblk + w - 1) / w;
-        if (pa::grouped_span_pieces(span, bp) <= pa::grouped_max_pieces(columns) &&
-            span <= 0x7fffffffLL) {
-            parts->span_blocks = (int)span;
-            parts->span_count = (int)((nblk + span - 1) / span);
-            return;
-        }
-    }
-    parts->span_blocks = parts->per_group * bp;  // whole partitions, aligned
-    parts->span_count = (parts->max_parts + parts->per_group - 1) / parts->per_group;
+    if (w < 1) w = 1;
+    const long long span = nblk > 0 ? (nblk + w - 1) / w : 1;
+    parts->span_blocks = (int)span;  // <= nblk <= INT_MAX / 16
+    parts->span_count = nblk > 0 ? (int)((nblk + span - 1) / span) : 1;
 }
 
 // Kernel selection of decode_v1 / decode_v2 (their tiles argument):
@@ -401,8 +392,7 @@ pa_status_t decode_v2(void *out, V2Run run, int *entry_tokens_out, const void *q
     // prefill kernel, and not when the per-partition partials were asked for).
     const bool grouped = run != V2Run::kPartitions && tiles <= 0 && parts.per_group > 1;
     if (grouped) {
-        const int columns = (int)std::min<long long>(16, (long long)(num_q_heads / num_kv_heads) * q_len);
-        grouped_spans(num_seqs, num_kv_heads * chunks, max_seq_len, columns, &parts);
+        grouped_spans(num_seqs, num_kv_heads * chunks, max_seq_len, &parts);
     }
     if (entry_tokens_out)
         *entry_tokens_out = grouped ? parts.span_blocks * kBlockTokens : partition_size;
@@ -422,6 +412,7 @@ pa_status_t decode_v2(void *out, V2Run run, int *entry_tokens_out, const void *q
             // partial each; Phase 2 merges those.
             st = from_hip(pa::launch_grouped(pb, parts, hs));
             parts.entry_tokens = parts.span_blocks * kBlockTokens;
+            parts.marked_entries = parts.span_count;  // every entry of the grid written
         } else {
             st = from_hip(pa::launch_partitions(pb, parts, hs));
         }

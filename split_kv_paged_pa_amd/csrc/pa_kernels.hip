@@ -141,10 +141,6 @@ template <> struct Mma<float> {
 };
 
 constexpr int kMergeCap = 2048;  // group partials (heads x groups) one fused merge can weigh
-// Piece slots of a kGrouped workgroup, counted at 16 columns: per-piece wave states
-// in LDS, 4 x 4 waves x 16 columns x 132 floats = 132 KiB at D = 128, of gfx950's
-// 160 KiB; stored column-compact, so 8 columns hold 8 slots.
-constexpr int kGroupedSlots16 = 4;
 
 
 // ---------------------------------------------------------------------------
@@ -233,7 +229,7 @@ __device__ __forceinline__ void merge_groups(const float *__restrict__ tmp_out,
 }
 
 // ---------------------------------------------------------------------------
-// Three schedules of one kernel (MODE):
+// Four schedules of one kernel (MODE):
 //   kPartials (V2 Phase 1): workgroup (pg, kv head, sequence) handles the
 //     partitions p in [pg * ppw, min((pg + 1) * ppw, ceil(L / P))) of that
 //     sequence and kv head, one after the other, and writes each one's partials.
@@ -245,19 +241,16 @@ __device__ __forceinline__ void merge_groups(const float *__restrict__ tmp_out,
 //     and writes the output.
 //   kSinglePass (V1): workgroup (0, kv head, sequence) covers the whole sequence
 //     as a single partition and writes the output.
-//   kGrouped (V2 Phase 1 when a workgroup takes several partitions, at most
-//     kMaxGroupedParts): the same partitions, each computed and merged across the
-//     waves exactly as in kPartials and folded, in order, into one group partial
-//     per head with the Phase-2 rescale (as kFused does); the workgroup writes
-//     that group partial -- normalised like a partition partial, with its exp-sum
-//     and max logit -- to entry blockIdx.x of the workspace, and Phase 2 merges
-//     ceil(parts / ppw) entries per row.  At a partition boundary each wave only
-//     deposits its state {max, exp-sum, output} for that partition in LDS, with
-//     no barrier; the cross-wave merges and the fold run once, after the
-//     workgroup's last block.  Every close a workgroup made mid-stream used to
-//     stall its waves at three barriers while their loads ran one block ahead
-//     (measured on the 100K-token workload: ~0.5-0.9 us per close), and its
-//     stores were ~0.7 us more.
+//   kGrouped (V2 Phase 1 when partitions are few): workgroup (x, kv head,
+//     sequence) takes the equal span of blocks [x * span, (x + 1) * span) of the
+//     row as its one partition, whatever partition boundaries of the caller's
+//     size fall inside it, and writes that span's partials to entry x; Phase 2
+//     merges the entries as partitions of 16 * span tokens.  An empty span
+//     (past the end of a shorter sequence) writes max logit -inf to its entry,
+//     so Phase 2 can take every entry of the grid without reading seq_lens.
+//     Closing the caller's partitions inside a span (each wave depositing its
+//     state at every boundary, all merged at the end) measured 0.6-1.0 us per
+//     100K-token step slower, for results that differ only in rounding.
 // ---------------------------------------------------------------------------
 enum Mode { kSinglePass = 0, kPartials = 1, kFused = 2, kGrouped = 3 };
 
@@ -270,10 +263,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
     T *__restrict__ out, int span_blocks) {
     constexpr bool kFinal = MODE == kSinglePass;
-    // kFused folds each partition into the workgroup's group partial at its close;
-    // kGrouped deposits per-partition wave states (KP slots) and folds at the end.
+    // kFused folds each partition into the workgroup's group partial at its close.
     constexpr bool kFold = MODE == kFused;
-    constexpr int KP = MODE == kGrouped ? kGroupedSlots16 : 1;
+    constexpr int KP = 1;
     using M = Mma<T>;
     constexpr int E = M::E;
     using VU = typename M::VU;
@@ -281,9 +273,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     constexpr int NT = D / 16;               // d tiles: value units and accumulator tiles
     constexpr int LDS_STRIDE = D + 4;
 
-    // Per (piece slot, wave, column) states: max, exp-sum, merge factor, output.
-    // kGrouped indexes them column-compact, row (k * NW + w) * ncol + g, so a
-    // workgroup holds KP * 16 / ncol piece slots (8 at 8 columns).
+    // Per (wave, column) states: max, exp-sum, merge factor, output (33 KiB at D = 128).
     __shared__ float sm_m[KP][NW][16];
     __shared__ float sm_l[KP][NW][16];
     __shared__ float sm_f[KP][NW][16];
@@ -294,10 +284,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     __shared__ float sm_gw[GA];
     __shared__ float sm_gs[GA];  // rescale of sm_ga for the partition being folded in
     __shared__ __attribute__((aligned(16))) float sm_ga[GA][kFold ? D : 1];
-    // kGrouped: rescale of the group partial before piece slot k is folded in
-    // (index k * ncol + g), and the group's exp-sum.
-    __shared__ float sm_ks[KP][16];
-    __shared__ float sm_kw[MODE == kGrouped ? 16 : 1];
     __shared__ uint32_t sm_ticket;
 
     const int lane = threadIdx.x & 63;
@@ -338,9 +324,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     // Partitions of this workgroup, in blocks of bp each.
     // The workgroup's blocks [b_lo, b_hi) fall in partitions p_begin .. p_end - 1;
     // piece p of them is [max(p * bp, b_lo), min((p + 1) * bp, b_hi)).  kGrouped
-    // takes span_blocks blocks from pg * span_blocks, whatever the partition
-    // boundaries (a partition cut by the span is finished by Phase 2's merge);
-    // the other modes take ppw whole partitions.
+    // takes span_blocks blocks from pg * span_blocks as one piece (the span is
+    // this workgroup's partition); the other modes take ppw whole partitions.
     int bp, p_begin, p_end, b_lo, b_hi;
     if (kFinal) {
         bp = max(nblk, 1);
@@ -349,12 +334,23 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         b_lo = 0;
         b_hi = nblk;
     } else if (MODE == kGrouped) {
-        bp = partition_size / kBlockTokens;
+        bp = span_blocks;
         b_lo = pg * span_blocks;
         b_hi = min(b_lo + span_blocks, nblk);
-        if (b_lo >= b_hi) return;  // uniform: past the sequence's last block
-        p_begin = b_lo / bp;
-        p_end = (b_hi - 1) / bp + 1;
+        if (b_lo >= b_hi) {  // uniform: past the sequence's last block
+            // Mark the entry empty (max logit -inf): Phase 2 then takes every
+            // entry of the grid without reading seq_lens first.
+            const int nc = min(16, group * qlen - c0);
+            if ((int)threadIdx.x < nc) {
+                const int c = c0 + (int)threadIdx.x;
+                const size_t row =
+                    ((size_t)s * qlen + c / group) * num_q_heads + (size_t)kvh * group + c % group;
+                store_through(max_logits + row * max_parts + pg, -INFINITY);
+            }
+            return;
+        }
+        p_begin = pg;
+        p_end = pg + 1;
     } else {
         bp = partition_size / kBlockTokens;
         const int parts = (nblk + bp - 1) / bp;
@@ -544,47 +540,30 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         }
     };
 
-    // kGrouped slot rows (column-compact): state row r = (k * NW + w) * ncol + g.
-    float *const fm = &sm_m[0][0][0];
-    float *const fl = &sm_l[0][0][0];
-    float *const ff = &sm_f[0][0][0];
-    float *const fo = &sm_o[0][0][0][0];
-    float *const fks = &sm_ks[0][0];
-
-    // End of piece p: merge the waves' states (fixed order) and write (or, kFold,
-    // fold them into the group partial).  kGrouped: deposit this wave's state in
-    // piece slot p - p_begin, without a barrier (merged at the end).
+    // End of piece p: merge the waves' states (fixed order) and write them (or,
+    // kFold, fold them into the group partial).
     auto finish = [&](int p) {
         const float l_col = column_sum(l_run);
-        if (MODE == kGrouped) {
-            // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of head g.
-            if (g < ncol) {
-                const int r = ((p - p_begin) * NW + w) * ncol + g;
-                if (grp == 0) {
-                    fm[r] = m_run;
-                    fl[r] = l_col;
-                }
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    *reinterpret_cast<f32x4 *>(fo + r * LDS_STRIDE + 16 * t + 4 * grp) = acc[t];
-            }
-        } else {
-            __syncthreads();  // the previous partition's readers are done
-            if (grp == 0) {
-                sm_m[0][w][g] = m_run;
-                sm_l[0][w][g] = l_col;
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *reinterpret_cast<f32x4 *>(&sm_o[0][w][g][16 * t + 4 * grp]) = acc[t];
+        if (p != p_begin) __syncthreads();  // the previous partition's readers are done
+        // acc[t] of lane (g, grp) holds d = 16t + 4*grp + [0, 4) of column g.
+        if (grp == 0) {
+            sm_m[0][w][g] = m_run;
+            sm_l[0][w][g] = l_col;
         }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4 *>(&sm_o[0][w][g][16 * t + 4 * grp]) = acc[t];
         m_run = -INFINITY;
         l_run = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (MODE == kGrouped) return;
         __syncthreads();
         // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
+        // The partition's exp-sum and max logit are stored after the next barrier:
+        // a barrier's release fence waits until the wave's earlier global stores
+        // have completed, a write-through round trip to memory (~1 us).
+        float st_sum = 0.f, st_max = 0.f;
+        bool st_ml = false;
         if (threadIdx.x < 16) {
             const int gg = threadIdx.x;
             float mx = -INFINITY;
@@ -614,9 +593,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) sm_f[0][ww][gg] = f[ww] * inv;
                 if (!kFinal && gg < ncol) {
-                    const size_t row = qrow_of(gg) * max_parts + p;
-                    store_through(exp_sums + row, total);
-                    store_through(max_logits + row, mx);
+                    st_ml = true;
+                    st_sum = total;
+                    st_max = mx;
                 }
             }
         }
@@ -641,6 +620,11 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + p) * D; },
                            gg, d, o);
             }
+        }
+        if (st_ml) {
+            const size_t row = qrow_of(threadIdx.x) * max_parts + p;
+            store_through(exp_sums + row, st_sum);
+            store_through(max_logits + row, st_max);
         }
     };
 
@@ -674,67 +658,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     }
     while (a_p < p_end) finish(a_p++);
 
-    if (MODE == kGrouped) {
-        // Merge each partition's deposited wave states across the waves and fold
-        // the partitions, in order, into the group partial -- per column, the
-        // same arithmetic as the kFused close: M' = max(M, m_p), W = W a + s_p b
-        // with a = exp(M - M'), b = exp(m_p - M') -- then write it, normalised,
-        // to entry blockIdx.x of the row.
-        const int np = p_end - p_begin;  // 1 .. KP * 16 / ncol pieces, uniform
-        __syncthreads();
-        if (threadIdx.x < ncol) {
-            const int gg = threadIdx.x;
-            float gm = -INFINITY, gw = 0.f;
-            for (int k = 0; k < np; ++k) {
-                const int r0 = k * NW * ncol + gg;  // row of wave 0; wave ww at r0 + ww * ncol
-                float mx = -INFINITY;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, fm[r0 + ww * ncol]);
-                float f[NW];
-                float total = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) {
-                    f[ww] = (mx == -INFINITY) ? 0.f : exp_e(fm[r0 + ww * ncol] - mx);
-                    total += f[ww] * fl[r0 + ww * ncol];
-                }
-                const float gm_new = fmaxf(gm, mx);
-                const float a = gm == -INFINITY ? 0.f : exp_e(gm - gm_new);
-                const float b = mx == -INFINITY ? 0.f : exp_e(mx - gm_new);
-                gw = gw * a + total * b;
-                gm = gm_new;
-                fks[k * ncol + gg] = a;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) ff[r0 + ww * ncol] = f[ww] * b;
-            }
-            sm_kw[gg] = gw;
-            {
-                const size_t row = qrow_of(gg) * max_parts + blockIdx.x;
-                store_through(exp_sums + row, gw);
-                store_through(max_logits + row, gm);
-            }
-        }
-        __syncthreads();
-        constexpr int C4 = D / 4;
-        for (int idx = threadIdx.x; idx < ncol * C4; idx += NW * 64) {
-            const int gg = idx / C4;
-            const int d = (idx - gg * C4) * 4;
-            f32x4 ga = {0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < np; ++k) {
-                const int r0 = k * NW * ncol + gg;
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww)
-                    o += ff[r0 + ww * ncol] *
-                         *reinterpret_cast<const f32x4 *>(fo + (r0 + ww * ncol) * LDS_STRIDE + d);
-                ga = ga * fks[k * ncol + gg] + o;
-            }
-            const float W = sm_kw[gg];
-            ga = ga * (W > 0.f ? 1.f / W : 0.f);
-            store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + blockIdx.x) * D; },
-                       gg, d, ga);
-        }
-        return;
-    }
     if (MODE != kFused) return;
 
     // ---- kFused epilogue.  Group partial g of this workgroup goes to entry gi =
@@ -797,6 +720,17 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 // (With a branch per partition the compiler waited for each load before issuing
 // the next: one memory round trip per partition.)
 // ---------------------------------------------------------------------------
+// Entries of sequence s that Phase 2 merges.  marked >= 0: Phase 1 wrote every
+// entry below marked -- an empty one with max logit -inf, which the merge skips --
+// so the count needs no seq_lens load (one memory round trip less before the
+// partials can be requested); else ceil(L_s / entry_tokens).
+__device__ __forceinline__ int row_entries(const int32_t *__restrict__ seq_lens, int s,
+                                           int max_seq_len, int entry_tokens, int marked) {
+    if (marked >= 0) return marked;
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    return L > 0 ? (int)(((long long)L + entry_tokens - 1) / entry_tokens) : 0;
+}
+
 template <int DPL> struct RowPiece;
 template <> struct RowPiece<1> { typedef float type; };
 template <> struct RowPiece<2> { typedef float type __attribute__((ext_vector_type(2))); };
@@ -805,7 +739,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    int max_seq_len, int partition_size, int max_parts, int marked, T *__restrict__ out) {
     using M = Mma<T>;
     constexpr int NT = NW * 64;
     constexpr int DPL = D / 64;
@@ -823,8 +757,7 @@ __global__ __launch_bounds__(NW * 64) void reduce_kernel(
     const size_t head = (size_t)s * num_q_heads + h;
     T *orow = out + head * D;
 
-    const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    const int parts = row_entries(seq_lens, s, max_seq_len, partition_size, marked);
     const float *ml = max_logits + head * max_parts;
     const float *es = exp_sums + head * max_parts;
     const Piece *po = reinterpret_cast<const Piece *>(tmp_out + head * max_parts * D) + lane;
@@ -924,7 +857,7 @@ template <typename T, int D, int K>
 __global__ __launch_bounds__(256) void reduce_split_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    int max_seq_len, int partition_size, int max_parts, int marked, T *__restrict__ out) {
     __shared__ __attribute__((aligned(16))) f32x4 sm_acc[4][8];
     __shared__ float sm_w[4];
     const int tid = threadIdx.x;
@@ -939,8 +872,7 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
     const size_t head = (size_t)s * num_q_heads + h;
     const int d0 = x * kSplitCols + 4 * c;
 
-    const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    const int parts = row_entries(seq_lens, s, max_seq_len, partition_size, marked);
     const float *ml = max_logits + head * max_parts;
     const float *es = exp_sums + head * max_parts;
     const float *po = tmp_out + head * max_parts * D + d0;
@@ -1021,7 +953,7 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_rows,
-    int max_seq_len, int partition_size, int max_parts, T *__restrict__ out) {
+    int max_seq_len, int partition_size, int max_parts, int marked, T *__restrict__ out) {
     using M = Mma<T>;
     constexpr int DPL = D / 64;
     const int lane = threadIdx.x & 63;
@@ -1030,8 +962,7 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void reduce_rows_kernel(
     if (h >= num_rows) return;  // no barrier in this kernel
     const int s = blockIdx.y;
     const size_t row = (size_t)s * num_rows + h;
-    const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int parts = L > 0 ? (int)(((long long)L + partition_size - 1) / partition_size) : 0;
+    const int parts = row_entries(seq_lens, s, max_seq_len, partition_size, marked);
     const float *ml = max_logits + row * max_parts;
     const float *es = exp_sums + row * max_parts;
     typedef typename RowPiece<DPL>::type Piece;
@@ -1163,7 +1094,7 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
         dim3 grid((num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, num_seqs);
         reduce_rows_kernel<T, D, 8><<<grid, kRowsPerGroup * 64, 0, stream>>>(
             parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
-            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+            parts.partition_size, parts.max_parts, parts.marked_entries, static_cast<T *>(out));
         return hipGetLastError();
     }
     constexpr int kSlices = D / kSplitCols;
@@ -1173,16 +1104,18 @@ hipError_t launch_reduce_t(const int32_t *seq_lens, int num_seqs, int num_q_head
         if (entries <= 128)
             reduce_split_kernel<T, D, 4><<<grid, 256, 0, stream>>>(
                 parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads,
-                max_seq_len, parts.partition_size, parts.max_parts, static_cast<T *>(out));
+                max_seq_len, parts.partition_size, parts.max_parts, parts.marked_entries,
+                static_cast<T *>(out));
         else  // one round of loads for up to 256 partitions
             reduce_split_kernel<T, D, 8><<<grid, 256, 0, stream>>>(
                 parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads,
-                max_seq_len, parts.partition_size, parts.max_parts, static_cast<T *>(out));
+                max_seq_len, parts.partition_size, parts.max_parts, parts.marked_entries,
+                static_cast<T *>(out));
     } else {  // many rows: one 16-wave workgroup per row already spreads over the CUs
         dim3 grid(num_q_heads, num_seqs);
         reduce_kernel<T, D, kReduceWaves><<<grid, kReduceWaves * 64, 0, stream>>>(
             parts.tmp_out, parts.exp_sums, parts.max_logits, seq_lens, num_q_heads, max_seq_len,
-            parts.partition_size, parts.max_parts, static_cast<T *>(out));
+            parts.partition_size, parts.max_parts, parts.marked_entries, static_cast<T *>(out));
     }
     return hipGetLastError();
 }
@@ -1197,16 +1130,12 @@ hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream
     return dispatch_attend<kPartials>(pb, &parts, nullptr, stream);
 }
 
-int grouped_max_pieces(int columns) {
-    return columns >= 1 && columns <= 16 ? kGroupedSlots16 * 16 / columns : 0;
-}
-
 hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream) {
-    // Every span must touch at most grouped_max_pieces partitions (the LDS slots).
-    const int bp = parts.partition_size / kBlockTokens;
-    const int columns = min(16, pb.num_q_heads / pb.num_kv_heads * pb.qlen);
-    if (parts.span_blocks < 1 || parts.span_count < 1 ||
-        grouped_span_pieces(parts.span_blocks, bp) > grouped_max_pieces(columns))
+    // Entry x of a row is written by span x: the spans must fit the workspace
+    // rows and cover the longest sequence.
+    const long long nblk = ((long long)pb.max_seq_len + kBlockTokens - 1) / kBlockTokens;
+    if (parts.span_blocks < 1 || parts.span_count < 1 || parts.span_count > parts.max_parts ||
+        (long long)parts.span_blocks * parts.span_count < nblk)
         return hipErrorInvalidValue;
     return dispatch_attend<kGrouped>(pb, &parts, nullptr, stream);
 }

@@ -37,6 +37,9 @@ struct Partials {
     int span_count;  // launch_grouped: workgroups per (sequence, kv head, chunk)
     int entry_tokens;  // tokens behind each entry Phase 2 reads: partition_size after
                        // launch_partitions, 16 * span_blocks after launch_grouped
+    int marked_entries;  // >= 0: Phase 1 wrote entries [0, marked_entries) of every row
+                         // (launch_grouped: span_count; an empty span's max logit is -inf),
+                         // so Phase 2 needs no seq_lens; -1: ceil(L_s / entry_tokens) entries
 };
 
 // V1: one workgroup per (kv head, sequence) over the whole sequence -> out.
@@ -44,19 +47,12 @@ hipError_t launch_single_pass(const Problem &pb, void *out, hipStream_t stream);
 // V2 Phase 1: one workgroup per (partition, kv head, sequence) -> partials.
 hipError_t launch_partitions(const Problem &pb, const Partials &parts, hipStream_t stream);
 // V2 Phase 1 as equal spans: workgroup x of a (sequence, kv head, chunk) takes
-// blocks [x * span_blocks, (x + 1) * span_blocks), computes each partition piece
-// in it, folds the pieces (the Phase-2 rescale) and writes one entry x of the
-// row -> Phase 2 then runs with entry_tokens = 16 * span_blocks.  The span may
-// cut at most grouped_max_pieces(columns) partitions (columns = min(16, G *
-// qlen)).
+// blocks [x * span_blocks, (x + 1) * span_blocks) as one partition and writes its
+// partials to entry x of the row (max logit -inf when the span is past the
+// sequence's end) -> Phase 2 then runs with entry_tokens = 16 * span_blocks and
+// marked_entries = span_count.  Needs span_count <= max_parts and span_count *
+// span_blocks >= ceil(max_seq_len / 16).
 hipError_t launch_grouped(const Problem &pb, const Partials &parts, hipStream_t stream);
-int grouped_max_pieces(int columns);
-// Most partitions (of bp blocks) that a span of span_blocks blocks starting at a
-// multiple of span_blocks can touch: span / bp when the spans are aligned to the
-// partitions, else one more than a span that starts at a boundary.
-inline long long grouped_span_pieces(long long span_blocks, int bp) {
-    return span_blocks % bp == 0 ? span_blocks / bp : (span_blocks - 1 + bp - 1) / bp + 1;
-}
 // V2 in one launch: the Phase-1 grid; each workgroup folds its partitions into a
 // group partial, and the last workgroup of each (sequence, kv head) merges them -> out.
 // Needs group * ceil(max_parts / per_group) <= fused_merge_capacity().

@@ -69,19 +69,23 @@ def test_many_partitions_reduce_chunks():
 
 
 GROUPED = [  # S * Hkv * ceil(max_len / P) between one and four units per compute unit
-    # (on 256 CUs: 2, 3, 4, 4 and 4 partitions per workgroup)
-    ("one_seq_p512", [20000], 8, 512),
-    ("one_seq_p256", [20000], 8, 256),
-    ("ragged_p256", [20000, 5, 13000], 4, 256),
-    ("ragged_p1024", [100000, 17, 65536, 1], 2, 1024),
-    ("one_seq_100k_p512", [100000], 4, 512),
+    # (on 256 CUs: spans of 2, 3, 4, 4, 4 and 4 partitions' length); name, lens, Hkv,
+    # GQA group, P.  The last case, 16 columns, is cut into 85 spans of 65 blocks
+    # per row: each span starts and ends inside one of the caller's 16-block
+    # partitions.
+    ("one_seq_p512", [20000], 8, 8, 512),
+    ("one_seq_p256", [20000], 8, 8, 256),
+    ("ragged_p256", [20000, 5, 13000], 4, 8, 256),
+    ("ragged_p1024", [100000, 17, 65536, 1], 2, 8, 1024),
+    ("one_seq_100k_p512", [100000], 4, 8, 512),
+    ("unaligned_spans_g16", [87296, 87296, 86000], 1, 16, 256),
 ]
 
 
-@pytest.mark.parametrize("name,lens,hkv,P", GROUPED, ids=[g[0] for g in GROUPED])
-def test_grouped_partitions(name, lens, hkv, P):
+@pytest.mark.parametrize("name,lens,hkv,group,P", GROUPED, ids=[g[0] for g in GROUPED])
+def test_grouped_partitions(name, lens, hkv, group, P):
     """Phase-1 workgroups that handle several consecutive partitions each."""
-    spec = wl.custom(name, 112, "bf16", hkv * 8, hkv, 128, lens)
+    spec = wl.custom(name, 112, "bf16", hkv * group, hkv, 128, lens)
     b = wl.generate(spec)
     db = DeviceBatch(b)
     print(f"[case] grouped {name}", flush=True)
@@ -100,19 +104,21 @@ def test_grouped_partitions(name, lens, hkv, P):
         assert_close(tmp[s, :, :n], rtmp[s, :, :n], "bf16", f"grouped partials s={s}")
 
 
-@pytest.mark.parametrize("name,lens,hkv,P", GROUPED, ids=[g[0] for g in GROUPED])
-def test_grouped_entries(name, lens, hkv, P):
+@pytest.mark.parametrize("name,lens,hkv,group,P", GROUPED, ids=[g[0] for g in GROUPED])
+def test_grouped_entries(name, lens, hkv, group, P):
     """Phase 1 as pa_decode_v2 runs it (pa_decode_v2_groups): with few partitions,
     equal spans of entry_tokens tokens, each entry the partial of the span's tokens
     -- compared with the oracle's partials at partition size entry_tokens.  Then
     Phase 2 over those entries reproduces pa_decode_v2 bit for bit."""
-    spec = wl.custom(name, 112, "bf16", hkv * 8, hkv, 128, lens)
+    spec = wl.custom(name, 112, "bf16", hkv * group, hkv, 128, lens)
     b = wl.generate(spec)
     db = DeviceBatch(b)
     ws = db.workspace(P)
     et = pa.pa_decode_v2_groups(*db.args(), P, ws)
     print(f"[case] grouped entries {name}: {et} tokens per entry", flush=True)
     assert et % 16 == 0 and et != P, "these shapes take equal spans on 256 CUs"
+    if name.startswith("unaligned"):
+        assert et == 65 * 16, "85 spans of 65 blocks"
     tmp, es, ml = (to_f64(x) for x in pa.workspace_views(ws, spec.num_seqs, spec.num_q_heads,
                                                          spec.head_dim, db.max_seq_len, P))
     q, kc, vc, bt, sl = b.numpy()
@@ -123,6 +129,9 @@ def test_grouped_entries(name, lens, hkv, P):
         assert np.all(np.abs(ml[s_, :, :n] - rml[s_, :, :n]) <= 1e-5 * (1 + np.abs(rml[s_, :, :n])))
         assert np.all(np.abs(es[s_, :, :n] - res[s_, :, :n]) <= 1e-2 * res[s_, :, :n])
         assert_close(tmp[s_, :, :n], rtmp[s_, :, :n], "bf16", f"span entries s={s_}")
+        # The spans past a shorter sequence's end mark their entries empty.
+        spans = oracle.num_partitions(db.max_seq_len, et)
+        assert np.all(ml[s_, :, n:spans] == -np.inf)
     out = db.new_out()
     pa.pa_decode_v2_reduce_entries(out, db.seq_lens, db.max_seq_len, P, et, ws)
     ref = db.run_v2(P)
