@@ -254,14 +254,22 @@ __device__ __forceinline__ void merge_groups(const float *__restrict__ tmp_out,
 // ---------------------------------------------------------------------------
 enum Mode { kSinglePass = 0, kPartials = 1, kFused = 2, kGrouped = 3 };
 
+// Argument order: what the first key/value loads depend on comes first -- the
+// block table and seq_lens, the table stride, the workgroup's block stride, the
+// caches and what forms their addresses (14 dwords) -- so that with kernel-
+// argument preloading (the first 14 dwords arrive in SGPRs at wave launch) the
+// first memory round trip is the block ids, not the argument buffer.
 template <typename T, int D, int NW, int U, int MODE>
 __global__ __launch_bounds__(NW * 64) void attend_kernel(
-    const T *__restrict__ query, const T *__restrict__ key_cache, const T *__restrict__ value_cache,
-    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int num_kv_heads, int group, int qlen, int num_blocks, int max_blocks, int max_seq_len,
-    float scale, int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ seq_lens,
+    const T *__restrict__ key_cache, const T *__restrict__ value_cache, int max_blocks,
+    int wg_blocks, int num_kv_heads, int num_blocks, int group, int qlen,
+    const T *__restrict__ query, int num_q_heads, int max_seq_len, float scale,
+    int partition_size, int ppw, int max_parts, float *__restrict__ tmp_out,
     float *__restrict__ exp_sums, float *__restrict__ max_logits, uint32_t *__restrict__ tickets,
-    T *__restrict__ out, int span_blocks) {
+    T *__restrict__ out) {
+    // wg_blocks: blocks per workgroup (grid x): the span (kGrouped), ppw partitions
+    // (kPartials, kFused); unused by kSinglePass.
     constexpr bool kFinal = MODE == kSinglePass;
     // kFused folds each partition into the workgroup's group partial at its close.
     constexpr bool kFold = MODE == kFused;
@@ -316,16 +324,15 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     // the row), so the two scalar loads share one memory latency.
     const int32_t *bt = block_tables + (size_t)s * max_blocks;
     const int j_first = (kFinal ? 0
-                                : MODE == kGrouped ? pg * span_blocks
-                                                   : pg * ppw * (partition_size / kBlockTokens)) + w;
+                                : pg * wg_blocks) + w;
     const int id_first = max_blocks > 0 ? bt[min(j_first, max_blocks - 1)] : 0;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
     // Partitions of this workgroup, in blocks of bp each.
     // The workgroup's blocks [b_lo, b_hi) fall in partitions p_begin .. p_end - 1;
     // piece p of them is [max(p * bp, b_lo), min((p + 1) * bp, b_hi)).  kGrouped
-    // takes span_blocks blocks from pg * span_blocks as one piece (the span is
-    // this workgroup's partition); the other modes take ppw whole partitions.
+    // takes wg_blocks blocks from pg * wg_blocks as one piece (the span is this
+    // workgroup's partition); the other modes take ppw whole partitions.
     int bp, p_begin, p_end, b_lo, b_hi;
     if (kFinal) {
         bp = max(nblk, 1);
@@ -334,9 +341,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         b_lo = 0;
         b_hi = nblk;
     } else if (MODE == kGrouped) {
-        bp = span_blocks;
-        b_lo = pg * span_blocks;
-        b_hi = min(b_lo + span_blocks, nblk);
+        bp = wg_blocks;
+        b_lo = pg * wg_blocks;
+        b_hi = min(b_lo + wg_blocks, nblk);
         if (b_lo >= b_hi) {  // uniform: past the sequence's last block
             // Mark the entry empty (max logit -inf): Phase 2 then takes every
             // entry of the grid without reading seq_lens first.
@@ -1057,14 +1064,17 @@ hipError_t launch_attend(const Problem &pb, const Partials *parts, void *out, hi
     const int gx = kFinal ? 1 : MODE == kGrouped ? parts->span_count
                                                 : (parts->max_parts + ppw - 1) / ppw;
     dim3 grid(gx, pb.num_kv_heads * nchunk, pb.num_seqs);
+    const int wg_blocks = kFinal ? 0
+                          : MODE == kGrouped ? parts->span_blocks
+                                             : ppw * (parts->partition_size / kBlockTokens);
     attend_kernel<T, D, kWaves, prefetch_depth<T, D>(), MODE><<<grid, kWaves * 64, 0, stream>>>(
-        static_cast<const T *>(pb.query), static_cast<const T *>(pb.key_cache),
-        static_cast<const T *>(pb.value_cache), pb.block_tables, pb.seq_lens, pb.num_q_heads,
-        pb.num_kv_heads, group, pb.qlen, pb.num_blocks, pb.max_blocks, pb.max_seq_len, pb.scale,
-        kFinal ? kBlockTokens : parts->partition_size, ppw, kFinal ? 0 : parts->max_parts,
-        kFinal ? nullptr : parts->tmp_out, kFinal ? nullptr : parts->exp_sums,
-        kFinal ? nullptr : parts->max_logits, MODE == kFused ? parts->tickets : nullptr,
-        static_cast<T *>(out), MODE == kGrouped ? parts->span_blocks : 0);
+        pb.block_tables, pb.seq_lens, static_cast<const T *>(pb.key_cache),
+        static_cast<const T *>(pb.value_cache), pb.max_blocks, wg_blocks, pb.num_kv_heads,
+        pb.num_blocks, group, pb.qlen, static_cast<const T *>(pb.query), pb.num_q_heads,
+        pb.max_seq_len, pb.scale, kFinal ? kBlockTokens : parts->partition_size, ppw,
+        kFinal ? 0 : parts->max_parts, kFinal ? nullptr : parts->tmp_out,
+        kFinal ? nullptr : parts->exp_sums, kFinal ? nullptr : parts->max_logits,
+        MODE == kFused ? parts->tickets : nullptr, static_cast<T *>(out));
     return hipGetLastError();
 }
 
