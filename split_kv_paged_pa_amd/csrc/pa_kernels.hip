@@ -565,12 +565,56 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
-        // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M) l_w).
-        // The partition's exp-sum and max logit are stored after the next barrier:
-        // a barrier's release fence waits until the wave's earlier global stores
-        // have completed, a write-through round trip to memory (~1 us).
-        float st_sum = 0.f, st_max = 0.f;
-        bool st_ml = false;
+        constexpr int C4 = D / 4;
+        if (!kFold) {
+            // Merge factors per (wave, column): f = exp(m_w - M) / (sum_w exp(m_w - M)
+            // l_w), taken by every thread of the column from the deposited states (the
+            // same arithmetic in each, so one barrier per close; sharing them through
+            // LDS took a second barrier and round trip).  Each thread merges 4
+            // consecutive d of one column; a partition's output goes out with
+            // store_row4, then its exp-sum and max logit (no barrier follows them: a
+            // barrier's release fence waits until the wave's global stores have
+            // completed, a write-through round trip to memory, ~1 us).
+            for (int idx = threadIdx.x; idx < ncol * C4; idx += NW * 64) {
+                const int gg = idx / C4;
+                const int d = (idx - gg * C4) * 4;
+                float mw[NW], lw[NW];
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    mw[ww] = sm_m[0][ww][gg];
+                    lw[ww] = sm_l[0][ww][gg];
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, mw[ww]);
+                float f[NW];
+                float total = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    f[ww] = (mx == -INFINITY) ? 0.f : exp_e(mw[ww] - mx);
+                    total += f[ww] * lw[ww];
+                }
+                const float inv = total > 0.f ? 1.f / total : 0.f;
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww)
+                    o += (f[ww] * inv) * *reinterpret_cast<const f32x4 *>(&sm_o[0][ww][gg][d]);
+                if (kFinal) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) out[qrow_of(gg) * D + d + r] = M::from_float(o[r]);
+                } else {
+                    store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + p) * D; },
+                               gg, d, o);
+                    if (d == 0) {
+                        const size_t row = qrow_of(gg) * max_parts + p;
+                        store_through(exp_sums + row, total);
+                        store_through(max_logits + row, mx);
+                    }
+                }
+            }
+            return;
+        }
+        // kFold: thread g < 16 folds column g's merge into the group partial.
         if (threadIdx.x < 16) {
             const int gg = threadIdx.x;
             float mx = -INFINITY;
@@ -583,7 +627,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 f[ww] = (mx == -INFINITY) ? 0.f : exp_e(sm_m[0][ww][gg] - mx);
                 total += f[ww] * sm_l[0][ww][gg];
             }
-            if (kFold) {
+            {
                 // Fold (mx, total, sum_w f_w o_w) into the group partial with the
                 // Phase-2 rescale: weights exp(m - M') against the new group max M'.
                 const float gm = sm_gm[gg];
@@ -595,21 +639,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
                 sm_gs[gg] = a;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) sm_f[0][ww][gg] = f[ww] * b;
-            } else {
-                const float inv = total > 0.f ? 1.f / total : 0.f;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) sm_f[0][ww][gg] = f[ww] * inv;
-                if (!kFinal && gg < ncol) {
-                    st_ml = true;
-                    st_sum = total;
-                    st_max = mx;
-                }
             }
         }
         __syncthreads();
-        // Each thread merges 4 consecutive d of one column; a partition's output
-        // goes out with store_row4.
-        constexpr int C4 = D / 4;
         for (int idx = threadIdx.x; idx < ncol * C4; idx += NW * 64) {
             const int gg = idx / C4;
             const int d = (idx - gg * C4) * 4;
@@ -617,21 +649,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww)
                 o += sm_f[0][ww][gg] * *reinterpret_cast<const f32x4 *>(&sm_o[0][ww][gg][d]);
-            if (kFold) {
-                f32x4 &ga = *reinterpret_cast<f32x4 *>(&sm_ga[gg][d]);
-                ga = ga * sm_gs[gg] + o;  // same thread owns (gg, d .. d+3) every time
-            } else if (kFinal) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) out[qrow_of(gg) * D + d + r] = M::from_float(o[r]);
-            } else {
-                store_row4([&](int g0) { return tmp_out + (qrow_of(g0) * max_parts + p) * D; },
-                           gg, d, o);
-            }
-        }
-        if (st_ml) {
-            const size_t row = qrow_of(threadIdx.x) * max_parts + p;
-            store_through(exp_sums + row, st_sum);
-            store_through(max_logits + row, st_max);
+            f32x4 &ga = *reinterpret_cast<f32x4 *>(&sm_ga[gg][d]);
+            ga = ga * sm_gs[gg] + o;  // same thread owns (gg, d .. d+3) every time
         }
     };
 
