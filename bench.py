@@ -451,7 +451,7 @@ def main():
     alg_bytes, kv_bytes = phase1_bytes(spec, P, entry_tokens)
     achieved = alg_bytes / (p1_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, P)
-    mode = "kPartials" if entry_tokens == P else f"kGrouped, spans of {entry_tokens} tokens"
+    mode = f"as pa_decode_v2 runs it, entries of {entry_tokens} tokens"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],

@@ -183,7 +183,22 @@ pa_status_t carve(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Phase-1 spans for the grouped form (few work units: parts.per_group > 1).  Each
+// Equal spans serve a batch whose partitions make at most kGroupFewUnits
+// workgroups per compute unit, when each (sequence, kv head, column chunk) row
+// gets at least two spans (ny rows per sequence).  Also when the partitions make
+// exactly one workgroup per CU, as the library's own partition size does for a
+// few long rows: the spans then cut the same blocks and Phase 2 skips its
+// seq_lens round trip (measured on MI355X, the 100K-token step at P = 1568:
+// 36.4 us per partition against 36.0 us for the spans at P = 512, same run).
+bool use_spans(int num_seqs, int ny, int max_parts) {
+    int cus = compute_units();
+    if (cus <= 0) return false;
+    const long long rows = (long long)num_seqs * ny;
+    return rows * max_parts <= (long long)kGroupFewUnits * cus && 2 * rows <= cus &&
+           max_parts >= 2;
+}
+
+// Phase-1 spans for the grouped form (few work units: use_spans).  Each
 // of the ny (kv head, column chunk) rows of a sequence is split into W equal
 // spans of blocks, W = CUs / (num_seqs * ny) -- one workgroup per compute unit --
 // but at most max_parts (the entries a workspace row holds); each span is one
@@ -390,7 +405,8 @@ pa_status_t decode_v2(void *out, V2Run run, int *entry_tokens_out, const void *q
                            num_q_heads / num_kv_heads, q_len, dtype, parts.max_parts);
     // Few partitions: Phase 1 in equal spans, one entry per span (not on the
     // prefill kernel, and not when the per-partition partials were asked for).
-    const bool grouped = run != V2Run::kPartitions && tiles <= 0 && parts.per_group > 1;
+    const bool grouped = run != V2Run::kPartitions && tiles <= 0 &&
+                         use_spans(num_seqs, num_kv_heads * chunks, parts.max_parts);
     if (grouped) {
         grouped_spans(num_seqs, num_kv_heads * chunks, max_seq_len, &parts);
     }
