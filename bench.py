@@ -209,6 +209,99 @@ def hbm_probe(dev):
     return {"unit": "GB/s", **res}
 
 
+def timeline(dev, args):
+    """Per-workgroup timeline of K back-to-back V2 steps from the diagnostic build
+    libpa_decode_timeline.so (the same kernels with start / mid / end stamps on the
+    100 MHz constant clock, csrc/pa_timeline.h).  Prints one JSON object: per launch
+    (then the median over launches), in us from the first Phase-1 workgroup's
+    start: the spread of Phase-1 starts, Phase-1 wave-0 streaming ends (median,
+    p90, last), the close (end - streaming end, median), the last Phase-1 end,
+    Phase 2's first start, its partials' arrival (median, last) and its last
+    end, and the next step's first Phase-1 start; then the mean streaming end of
+    the workgroups on each XCD and the spread of each workgroup's end from launch
+    to launch.  The Phase-2 record's atomic adds one round trip to the end of
+    Phase 2, so the last interval and the step time run longer than in the
+    product library."""
+    import ctypes
+    from split_kv_paged_pa_amd import api
+    path = os.path.join(ROOT, "split_kv_paged_pa_amd", "libpa_decode_timeline.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: python split_kv_paged_pa_amd/build.py")
+    api._lib = None
+    api.LIB_PATH = path
+    lib = api.load_library()
+    lib.pa_timeline_fetch.restype = ctypes.c_int
+    lib.pa_timeline_fetch.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    spec = wl.config(args.workload)
+    batch = wl.generate(spec)
+    S, Hq, D, L = spec.num_seqs, spec.num_q_heads, spec.head_dim, spec.max_seq_len
+    P = args.partition_size or pa.pa_select_partition_size(S, spec.num_kv_heads, L)
+    q, bt, sl = batch.query.to(dev), batch.block_tables.to(dev), batch.seq_lens.to(dev)
+    kcs, vcs = [batch.key_cache.to(dev)], [batch.value_cache.to(dev)]
+    for _ in range(args.copies - 1):
+        kcs.append(kcs[0].clone())
+        vcs.append(vcs[0].clone())
+    out, stream = torch.empty_like(q), torch.cuda.current_stream()
+    ws = pa.new_workspace(S, Hq, D, L, P, device=dev)
+    calls = [pa.bind_decode_v2(out, q, kcs[c], vcs[c], bt, sl, spec.scale, L, P, ws, stream)
+             for c in range(len(kcs))]
+    n_rec = 1 << 18
+    buf = np.zeros((n_rec, 4), np.uint64)
+    for i in range(10):
+        calls[i % len(calls)]()
+    assert lib.pa_timeline_fetch(None, 0) >= 0  # clear
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.timeline):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = lib.pa_timeline_fetch(buf.ctypes.data, n_rec)
+    assert 0 <= n <= n_rec, f"timeline fetch failed or overflowed: {n}"
+    r = buf[:n].astype(np.int64)
+    r = r[(r[:, 0] & 15) != 0]  # holes: workgroups that had no work
+    kind, xcc, lin = r[:, 0] & 15, (r[:, 0] >> 4) & 15, (r[:, 0] >> 8) & 0xffffff
+    t = r[:, 1:4] / 100.0  # 10 ns ticks -> us
+    runs, a = [], 0  # consecutive records of one kind: one launch
+    for i in range(1, len(r) + 1):
+        if i == len(r) or kind[i] != kind[a]:
+            runs.append((int(kind[a]), a, i))
+            a = i
+    p1 = [x for x in runs if x[0] == 1]
+    p2 = [x for x in runs if x[0] == 2]
+    rows, ends = [], []
+    for k in range(min(len(p1), len(p2)) - 1):
+        _, a1, b1 = p1[k]
+        _, a2, b2 = p2[k]
+        T0 = t[a1:b1, 0].min()
+        s1, s2 = t[a1:b1] - T0, t[a2:b2] - T0
+        rows.append([s1[:, 0].max(), np.median(s1[:, 1]), np.percentile(s1[:, 1], 90), s1[:, 1].max(),
+                     np.median(s1[:, 2] - s1[:, 1]), s1[:, 2].max(), s2[:, 0].min(),
+                     np.median(s2[:, 1]), s2[:, 1].max(), s2[:, 2].max(),
+                     t[p1[k + 1][1]:p1[k + 1][2], 0].min() - T0])
+        o = np.argsort(lin[a1:b1])
+        ends.append(((t[a1:b1, 1] - T0)[o], xcc[a1:b1][o]))
+    names = ["p1_start_spread", "p1_stream_end_median", "p1_stream_end_p90", "p1_stream_end_last",
+             "p1_close_median", "p1_end_last", "p2_first_start", "p2_partials_median",
+             "p2_partials_last", "p2_end_last", "next_p1_start"]
+    R = np.array(rows)
+    res = {nm: round(float(np.median(R[:, j])), 2) for j, nm in enumerate(names)}
+    same = len({len(e[0]) for e in ends}) == 1
+    if same and ends:
+        E = np.array([e[0] for e in ends])
+        X = ends[0][1]
+        res["stream_end_mean_by_xcc"] = {int(x): round(float(E[:, X == x].mean()), 2)
+                                         for x in np.unique(X)}
+        resid = E - np.median(E, 1, keepdims=True)
+        res["workgroup_end_spread_std"] = round(float((resid - resid.mean(0)).std()), 2)
+    print(json.dumps({"timeline": res, "workload": spec.name, "partition_size": P,
+                      "launches": len(rows), "phase1_workgroups": int(p1[0][2] - p1[0][1]),
+                      "phase2_workgroups": int(p2[0][2] - p2[0][1]) if p2 else 0,
+                      "us_per_step_back_to_back": round(e0.elapsed_time(e1) * 1e3 / args.timeline, 2),
+                      "note": "diagnostic build (libpa_decode_timeline.so); us from the first "
+                              "Phase-1 workgroup's start, medians over launches"}), flush=True)
+
+
 DISPATCH_GRID = [(1, 1), (1, 8), (4, 8), (16, 8), (64, 8), (256, 8)]
 DISPATCH_LENS = [512, 1024, 2048, 4096, 8192, 16384]
 
@@ -286,6 +379,9 @@ def main():
     ap.add_argument("--extras", action="store_true",
                     help="also time V2 in a single launch, V2 with several query tokens per "
                          "sequence, and the tiled prefill kernel (same cache)")
+    ap.add_argument("--timeline", type=int, default=0, metavar="K",
+                    help="instead of the step benchmark, run K steps on the diagnostic timeline "
+                         "build and print the per-workgroup timeline summary")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="instead of the step benchmark, time V1 / V2 over a grid of batch shapes "
                          "and compare the two dispatch rules")
@@ -303,6 +399,9 @@ def main():
 
     if args.dispatch_sweep:
         dispatch_sweep(dev)
+        return
+    if args.timeline:
+        timeline(dev, args)
         return
     spec = wl.config(args.workload)
     batch = wl.generate(spec)

@@ -27,6 +27,9 @@ PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 SOURCES = [(os.path.join(CSRC, "pa_kernels.hip"), VGPR_FORM + PRELOAD),
            (os.path.join(CSRC, "pa_prefill.hip"), VGPR_FORM + PRELOAD),
            (os.path.join(CSRC, "pa_api.cpp"), [])]
+# Diagnostic copy of the same kernels with per-workgroup timestamps
+# (-DPA_TIMELINE, csrc/pa_timeline.h); read by bench.py --timeline only.
+TIMELINE_LIB = os.path.join(HERE, "libpa_decode_timeline.so")
 PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
 PROBE_SOURCES = [(os.path.join(CSRC, "pa_probe.hip"), VGPR_FORM)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,11 +46,11 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def _link(sources, lib, verbose, extra):
+def _link(sources, lib, verbose, extra, tag=""):
     os.makedirs(OBJ_DIR, exist_ok=True)
     objs = []
     for src, own in sources:
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + tag + ".o")
         _run([HIPCC, *FLAGS, *own, *extra, "-x", "hip", "-c", src, "-o", obj], verbose)
         objs.append(obj)
     tmp = lib + ".tmp"
@@ -57,9 +60,11 @@ def _link(sources, lib, verbose, extra):
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """libpa_decode.so (the attention ABI) and libpa_probe.so (bandwidth probe)."""
+    """libpa_decode.so (the attention ABI), libpa_probe.so (bandwidth probe) and
+    libpa_decode_timeline.so (the same kernels with timestamps, diagnostic)."""
     _link(SOURCES, LIB, verbose, extra)
     _link(PROBE_SOURCES, PROBE_LIB, verbose, extra)
+    _link(SOURCES, TIMELINE_LIB, verbose, (*extra, "-DPA_TIMELINE"), tag=".timeline")
     return LIB
 
 

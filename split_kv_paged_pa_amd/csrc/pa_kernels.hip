@@ -57,6 +57,7 @@
 
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_timeline.h"
 
 namespace pa {
 namespace {
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
     T *__restrict__ out) {
     // wg_blocks: blocks per workgroup (grid x): the span (kGrouped), ppw partitions
     // (kPartials, kFused); unused by kSinglePass.
+    PA_TL_BEGIN_SLOT();  // diagnostic timeline build only
     constexpr bool kFinal = MODE == kSinglePass;
     // kFused folds each partition into the workgroup's group partial at its close.
     constexpr bool kFold = MODE == kFused;
@@ -682,7 +684,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(
         }
         if (done) break;
     }
+    PA_TL_MARK(pa_tl_mid);
     while (a_p < p_end) finish(a_p++);
+    PA_TL_RECORD(1, pa_tl_mid);
 
     if (MODE != kFused) return;
 
@@ -884,6 +888,7 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
     const float *__restrict__ tmp_out, const float *__restrict__ exp_sums,
     const float *__restrict__ max_logits, const int32_t *__restrict__ seq_lens, int num_q_heads,
     int max_seq_len, int partition_size, int max_parts, int marked, T *__restrict__ out) {
+    PA_TL_BEGIN();  // diagnostic timeline build only
     __shared__ __attribute__((aligned(16))) f32x4 sm_acc[4][8];
     __shared__ float sm_w[4];
     const int tid = threadIdx.x;
@@ -945,6 +950,7 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
             }
         }
     }
+    PA_TL_MARK(pa_tl_mid);
     // Fold the eight partition slots of each d chunk: lanes c, c + 8, ..., c + 56.
 #pragma unroll
     for (int off = 8; off < 64; off <<= 1) {
@@ -963,6 +969,7 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(
         store_out4(out + head * D + x * kSplitCols, kSplitCols, lane, a[0] * inv, a[1] * inv,
                    a[2] * inv, a[3] * inv);
     }
+    PA_TL_RECORD_LATE(2, pa_tl_mid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1194,3 +1201,28 @@ hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads,
 }
 
 }  // namespace pa
+
+#ifdef PA_TIMELINE
+// Diagnostic timeline build: copies the records written so far (at most
+// max_records of 4 x uint64) to host memory dst, then clears them and the
+// counter.  Returns the number of records the counter reached (holes left by
+// workgroups that had no work are all-zero), or a negative value if a HIP call
+// failed.  Synchronises the device.
+extern "C" int pa_timeline_fetch(void *dst, int max_records) {
+    void *buf = nullptr, *cnt = nullptr;
+    if (hipGetSymbolAddress(&buf, HIP_SYMBOL(pa::g_timeline)) != hipSuccess ||
+        hipGetSymbolAddress(&cnt, HIP_SYMBOL(pa::g_timeline_count)) != hipSuccess)
+        return -1;
+    if (hipDeviceSynchronize() != hipSuccess) return -2;
+    unsigned n = 0;
+    if (hipMemcpy(&n, cnt, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) return -3;
+    unsigned m = n < pa::kTimelineRecords ? n : pa::kTimelineRecords;
+    if (max_records >= 0 && m > (unsigned)max_records) m = (unsigned)max_records;
+    if (dst && m && hipMemcpy(dst, buf, (size_t)m * 32, hipMemcpyDeviceToHost) != hipSuccess)
+        return -4;
+    if (hipMemset(buf, 0, (size_t)pa::kTimelineRecords * 32) != hipSuccess ||
+        hipMemset(cnt, 0, sizeof(n)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return -5;
+    return (int)n;
+}
+#endif

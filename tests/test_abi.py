@@ -31,6 +31,22 @@ def test_exports_every_declared_function():
         assert hasattr(lib, n), f"{n} declared in pa_decode.h but not exported"
 
 
+def test_timeline_library_exports():
+    """The diagnostic build exports everything pa_decode.h declares plus the
+    timeline fetch of pa_timeline.h; the product library does not export it."""
+    path = os.path.join(ROOT, "split_kv_paged_pa_amd", "libpa_decode_timeline.so")
+    if not os.path.exists(path):
+        pytest.skip("libpa_decode_timeline.so not built")
+    lib = ctypes.CDLL(path)
+    text = open(os.path.join(ROOT, "include", "pa_timeline.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    extra = sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    assert extra == ["pa_timeline_fetch"]
+    for n in declared_functions() + extra:
+        assert hasattr(lib, n), f"{n} not exported by libpa_decode_timeline.so"
+    assert not hasattr(pa.load_library(), "pa_timeline_fetch")
+
+
 def test_status_strings():
     for st in range(7):
         assert pa.pa_status_string(st).startswith("PA_")
