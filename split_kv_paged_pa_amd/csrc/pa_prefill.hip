@@ -222,14 +222,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         const char *base[4] = {kbase + o0, kbase + o1, vbase + o0, vbase + o1};  // uniform
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const char *src;
             if constexpr (kLoads == 4) {
-                src = base[i] + tid * 16;
+                // One slab per load: a buffer load from a wave-uniform descriptor
+                // at the thread's constant offset (no per-step address arithmetic).
+                st[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base[i]), 0, kSlab, kBufferWord3),
+                    tid * 16, 0, 0);
             } else {
                 const int hi = tid >= kPieces;
-                src = (hi ? base[2 * i + 1] : base[2 * i]) + (tid - hi * kPieces) * 16;
+                const char *src = (hi ? base[2 * i + 1] : base[2 * i]) + (tid - hi * kPieces) * 16;
+                st[i] = *reinterpret_cast<const u32x4 *>(src);
             }
-            st[i] = *reinterpret_cast<const u32x4 *>(src);
         }
     };
     // LDS positions (16-byte units) inside a region, chosen so that every group
@@ -291,6 +294,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                 for (int ks = 0; ks < KS; ++ks) a = mfma_bf16_32(kr[t][ks], qv[ct][ks], a);
                 sa[ct][t] = a;
             }
+        // Exponents of the weights against each column's reference: e = z log2 e - m
+        // (z = scale q.k), taken before the column maxima so that the maxima run on
+        // fma results, which need no NaN-quieting before each v_max.  A token the
+        // column does not see gets e = -inf.
+        auto masked = [&](int ct, int t, int i) { return !okb || t0 + 4 * t + i > lim[ct]; };
+        float e[NCT][2][4];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e[ct][t][i] = fmaf(sa[ct][t][i], c2, -m[ct]);
         if (!full) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -298,32 +313,58 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!okb || t0 + 4 * t + i > lim[ct]) sa[ct][t][i] = -INFINITY;
+                        if (masked(ct, t, i)) e[ct][t][i] = -INFINITY;
         }
-        // Column maxima; one wave-uniform branch covers the (rare) moves of the
-        // reference max of any tile.
-        float mx2[NCT];
+        // Column maxima of e.  The reference moves when some e exceeds kLazyLog2,
+        // which includes a column's first visible token (m = -inf gives e = +inf);
+        // one wave-uniform branch covers the (rare) moves of any tile.
+        auto col_max8 = [](const float (&v)[2][4]) {
+            return column_max(fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
+                                    fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3]))));
+        };
+        float mxe[NCT];
         bool grow_any = false;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 a = sa[ct][0], b = sa[ct][1];
-            const float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
-                                   fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
-            mx2[ct] = column_max(mx) * c2;
-            mt[ct] = fmaxf(mt[ct], mx2[ct]);
-            grow_any |= mx2[ct] > m[ct] + kLazyLog2;
+            mxe[ct] = col_max8(e[ct]);
+            grow_any |= mxe[ct] > kLazyLog2;
         }
         if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const bool grow = mx2[ct] > m[ct] + kLazyLog2;
-                const float alpha = !grow ? 1.f : (m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - mx2[ct]));
-                if (grow) m[ct] = mx2[ct];
-                accl[ct] *= alpha;
+                if (mxe[ct] > kLazyLog2) {  // the same for the four lanes of a column
+                    // New reference: the step's largest scaled logit, i.e. m + max e,
+                    // or -- for a column that had seen nothing -- the max over the
+                    // visible raw products, scaled.
+                    float m_new = m[ct] + mxe[ct];
+                    if (m[ct] == -INFINITY) {
+                        float raw[2][4];
 #pragma unroll
-                for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                raw[t][i] = (!full && masked(ct, t, i)) ? -INFINITY : sa[ct][t][i];
+                        m_new = col_max8(raw) * c2;
+                    }
+                    const float alpha = m[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[ct] - m_new);
+                    m[ct] = m_new;
+                    mxe[ct] = 0.f;  // the step's max, against the new reference
+                    accl[ct] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < DT; ++t) acc[ct][t] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            e[ct][t][i] = (!full && masked(ct, t, i)) ? -INFINITY
+                                                                      : fmaf(sa[ct][t][i], c2, -m_new);
+                }
             }
         }
+        // True max of the scaled logits (log2 units), for the partials: a column
+        // that saw nothing in this step has mxe = -inf and keeps mt.
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mt[ct] = fmaxf(mt[ct], m[ct] + mxe[ct]);
         // Values first (one masking branch), then per tile: weights, then its PV
         // MFMAs, so the exponentials of tile ct + 1 can run while the matrix
         // cores work on tile ct.
@@ -343,15 +384,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pr[t][i] = __builtin_amdgcn_exp2f(fmaf(sa[ct][t][i], c2, -m[ct]));
-            if (!full) {
-                // A column that has seen nothing keeps m = -inf: weights 0, not NaN.
-                const bool dead = m[ct] == -INFINITY;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pr[t][i] = dead ? 0.f : pr[t][i];
-            }
+                for (int i = 0; i < 4; ++i) pr[t][i] = __builtin_amdgcn_exp2f(e[ct][t][i]);  // 2^-inf = 0
             const uint4 pb = make_uint4(pack2_bf16(pr[0][0], pr[0][1]), pack2_bf16(pr[0][2], pr[0][3]),
                                         pack2_bf16(pr[1][0], pr[1][1]), pack2_bf16(pr[1][2], pr[1][3]));
 #pragma unroll
