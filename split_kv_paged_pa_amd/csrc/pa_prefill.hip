@@ -72,6 +72,21 @@ __device__ __forceinline__ f32x4 mfma_bf16_32(uint4 a, uint4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// max(a, b, c) in one v_max3_f32, max(a, b) in one v_max_f32.  The operands
+// here are fma results, -inf, or results of these (never signalling NaNs), so
+// the NaN-quieting the compiler puts before each operand of fmaxf in IEEE mode
+// is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // The first `keep` (0..8) bf16 values of v, the rest zeroed.
 __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
     auto word = [&](uint32_t x, int k) -> uint32_t {
@@ -183,7 +198,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // Steps of two blocks; none without any cache block (every id would be skipped).
     const int nsteps = num_blocks > 0 ? (je_g - jb + 1) / 2 : 0;
 
-    float m[NCT], mt[NCT];  // reference max, true max (log2 units)
+    // m: the column's reference max; mt: this lane's part of the true max (log2
+    // units), the maximum over the lane's own tokens, reduced over the column's
+    // four lanes after the last step.
+    float m[NCT], mt[NCT];
     f32x4 acc[NCT][DT];
     // Exp-sums: one more PV MFMA per tile against an all-ones A operand leaves
     // the column's sum of the (bf16) weights in every register of lane (n, q),
@@ -315,28 +333,35 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                     for (int i = 0; i < 4; ++i)
                         if (masked(ct, t, i)) e[ct][t][i] = -INFINITY;
         }
-        // Column maxima of e.  The reference moves when some e exceeds kLazyLog2,
-        // which includes a column's first visible token (m = -inf gives e = +inf);
-        // one wave-uniform branch covers the (rare) moves of any tile.
+        // The reference moves when some e of the column exceeds kLazyLog2, which
+        // includes a column's first visible token (m = -inf gives e = +inf).  The
+        // test runs on each lane's own maximum; only a step where some lane
+        // passes it (rare after the first) takes the column maxima across the
+        // four lanes, in one wave-uniform branch for all tiles.
+        auto lane_max8 = [](const float (&v)[2][4]) {
+            return max2f(max3f(max3f(max3f(v[0][0], v[0][1], v[0][2]), v[0][3], v[1][0]), v[1][1], v[1][2]),
+                         v[1][3]);
+        };
         auto col_max8 = [](const float (&v)[2][4]) {
             return column_max(fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
                                     fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3]))));
         };
-        float mxe[NCT];
-        bool grow_any = false;
+        float mxe[NCT];  // this lane's largest e
+        float mx_all = -INFINITY;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            mxe[ct] = col_max8(e[ct]);
-            grow_any |= mxe[ct] > kLazyLog2;
+            mxe[ct] = lane_max8(e[ct]);
+            mx_all = ct == 0 ? mxe[0] : max2f(mx_all, mxe[ct]);
         }
-        if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
+        if (__builtin_amdgcn_ballot_w64(mx_all > kLazyLog2) != 0) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                if (mxe[ct] > kLazyLog2) {  // the same for the four lanes of a column
+                const float cmx = column_max(mxe[ct]);  // the column's largest e
+                if (cmx > kLazyLog2) {  // the same for the four lanes of a column
                     // New reference: the step's largest scaled logit, i.e. m + max e,
                     // or -- for a column that had seen nothing -- the max over the
                     // visible raw products, scaled.
-                    float m_new = m[ct] + mxe[ct];
+                    float m_new = m[ct] + cmx;
                     if (m[ct] == -INFINITY) {
                         float raw[2][4];
 #pragma unroll
@@ -361,10 +386,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
                 }
             }
         }
-        // True max of the scaled logits (log2 units), for the partials: a column
-        // that saw nothing in this step has mxe = -inf and keeps mt.
+        // True max of the scaled logits (log2 units), for the partials: a lane
+        // that saw nothing in this step has mxe = -inf and keeps mt.  (Rounding
+        // of m + x is monotonic in x, so the column's maximum over its lanes
+        // equals m + the column's largest e.)
+        if constexpr (!kFinal) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) mt[ct] = fmaxf(mt[ct], m[ct] + mxe[ct]);
+            for (int ct = 0; ct < NCT; ++ct) mt[ct] = fmaxf(mt[ct], m[ct] + mxe[ct]);
+        }
         // Values first (one masking branch), then per tile: weights, then its PV
         // MFMAs, so the exponentials of tile ct + 1 can run while the matrix
         // cores work on tile ct.
@@ -434,6 +463,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const float lc = accl[ct][0];  // the column's exp-sum (all four registers hold it)
+        if constexpr (!kFinal) mt[ct] = column_max(mt[ct]);
         const int c = cw + 16 * ct + n;
         if (c >= ncols) continue;
         const float inv = lc > 0.f ? 1.f / lc : 0.f;
