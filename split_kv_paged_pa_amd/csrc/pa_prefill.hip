@@ -87,6 +87,16 @@ __device__ __forceinline__ float max2f(float a, float b) {
     return r;
 }
 
+// 16 bytes per lane from `slab` (bytes in range) at byte `voffset` into LDS at
+// `dst` + 16 * lane (dst wave-uniform): a buffer load with the lds flag, which
+// writes LDS itself and counts in vmcnt.  (A __device__ function, not a lambda:
+// the host pass of a kernel's lambdas must not see this builtin.)
+__device__ __forceinline__ void load_lds16(const char *slab, int bytes, int voffset, char *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(slab), 0, bytes, kBufferWord3), dst, 16, voffset, 0,
+        0, 0);
+}
+
 // The first `keep` (0..8) bf16 values of v, the rest zeroed.
 __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
     auto word = [&](uint32_t x, int k) -> uint32_t {
@@ -124,7 +134,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     constexpr int kRegion = kSlab + 128;
     constexpr int kStage = 4 * kRegion;
     constexpr int kStages = 3;
-    __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+    // One array per stage: the compiler tracks the loads that write LDS per
+    // array, so reading one stage waits only for the loads into that stage
+    // (with one array it would wait for every load in flight).
+    static_assert(kStages == 3, "the step loop is unrolled by the stage count");
+    __shared__ __attribute__((aligned(16))) char lds0[kStage];
+    __shared__ __attribute__((aligned(16))) char lds1[kStage];
+    __shared__ __attribute__((aligned(16))) char lds2[kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -230,48 +246,39 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         if ((unsigned)id0 >= (unsigned)num_blocks) id0 = -1;
         if ((unsigned)id1 >= (unsigned)num_blocks) id1 = -1;
     };
-    // Piece k = tid + 256 i of a step: region r = k / kPieces (keys of block 0,
-    // keys of block 1, values of block 0, values of block 1), piece k % kPieces.
-    // With D = 128 load i is region i; with D = 64 it is region 2i + tid / 128.
+    // A step's 4 slabs (keys of blocks j, j + 1, then their values) go straight
+    // from global memory into an LDS stage (buffer loads with the lds flag: the
+    // data is written to LDS by the load itself, with no register staging and no
+    // LDS store instruction in the wave).  Such a load writes 16 bytes per lane
+    // at consecutive positions: lane l of wave w, load i, fills position
+    // p = (256 i + 64 w + l) % kPieces of region r = (256 i + 64 w + l) / kPieces
+    // (D = 128: region i; D = 64: region 2i + w / 2).  Positions are permuted at
+    // 16-byte granularity so that every group of 8 (and of 16) lanes of an
+    // operand read touches distinct banks; position p of a region holds piece
+    // swz(p) of its slab (swz is its own inverse):
+    //   keys, piece (chunk c, token t) at 16c + (t ^ 4 * (t / 8));
+    //   values, piece x (row x / 2, token half x % 2) at x ^ ((x / 8 ^ x / 16) & 1).
     // A block that is not attended is replaced by block 0 of the same kv head
     // (valid memory; its tokens are masked), so every step issues the same loads.
-    auto fetch = [&](int id0, int id1, u32x4 (&st)[kLoads]) {
-        const size_t o0 = (size_t)max(id0, 0) * blk_stride, o1 = (size_t)max(id1, 0) * blk_stride;
-        const char *base[4] = {kbase + o0, kbase + o1, vbase + o0, vbase + o1};  // uniform
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            if constexpr (kLoads == 4) {
-                // One slab per load: a buffer load from a wave-uniform descriptor
-                // at the thread's constant offset (no per-step address arithmetic).
-                st[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base[i]), 0, kSlab, kBufferWord3),
-                    tid * 16, 0, 0);
-            } else {
-                const int hi = tid >= kPieces;
-                const char *src = (hi ? base[2 * i + 1] : base[2 * i]) + (tid - hi * kPieces) * 16;
-                st[i] = *reinterpret_cast<const u32x4 *>(src);
-            }
-        }
-    };
-    // LDS positions (16-byte units) inside a region, chosen so that every group
-    // of 8 (and of 16) lanes of an operand read touches distinct banks:
-    //   keys, piece (chunk c, token t) -> 16c + (t ^ 4 * (t / 8));
-    //   values, piece x (row x / 2, token half x % 2) -> x ^ ((x / 8 ^ x / 16) & 1).
-    int st_off[kLoads];  // LDS byte offset of this thread's piece i inside a stage
+    int dma_lds[kLoads], dma_src[kLoads];  // LDS byte offset of the wave's run, lane's source byte
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const int k = tid + NW * 64 * i;
         const int r = k / kPieces;
-        const int pc = k - r * kPieces;
-        const int pos = r < 2 ? (pc ^ (((pc >> 3) & 1) << 2)) : (pc ^ (((pc >> 3) ^ (pc >> 4)) & 1));
-        st_off[i] = r * kRegion + pos * 16;
+        const int pos = k - r * kPieces;
+        const int pc = r < 2 ? (pos ^ (((pos >> 3) & 1) << 2)) : (pos ^ (((pos >> 3) ^ (pos >> 4)) & 1));
+        dma_lds[i] = __builtin_amdgcn_readfirstlane(r * kRegion + (pos - lane) * 16);
+        dma_src[i] = pc * 16;  // byte offset inside the slab
     }
-    auto stash = [&](int stage, const u32x4 (&st)[kLoads]) {
-        char *dst = lds + stage * kStage;
+    auto dma = [&](char *stage, int id0, int id1) {
+        const size_t o0 = (size_t)max(id0, 0) * blk_stride, o1 = (size_t)max(id1, 0) * blk_stride;
+        const char *base[4] = {kbase + o0, kbase + o1, vbase + o0, vbase + o1};  // uniform
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4 *>(dst + st_off[i]) = st[i];
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = (kLoads == 4) ? i : 2 * i + (w >> 1);  // uniform
+            load_lds16(base[r], kSlab, dma_src[i], stage + dma_lds[i]);
+        }
     };
-
     // LDS offsets of the operands.  Keys [D/8][16][8]: A row n of tile T is token
     // t = 8b + 4T + n%4 (b = (n/4)%2) of block n/8, d chunk 4 ks + q, stored at
     // token slot t ^ 4b = 8b + 4(T ^ b) + n%4.  Values [D][16]: lane (n, q) reads
@@ -285,12 +292,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     const int vx = 2 * n + (q & 1);
     const int v_lds = (2 + (q >> 1)) * kRegion + (vx ^ (((vx >> 3) ^ (vx >> 4)) & 1)) * 16;
 
-    // One step of 32 tokens from LDS stage `stage`: logits, reference update,
+    // One step of 32 tokens from an LDS stage: logits, reference update,
     // weights, PV.
-    auto step = [&](int j, int stage, bool ok0, bool ok1) {
-        const char *sk0 = lds + stage * kStage + k_lds0;
-        const char *sk1 = lds + stage * kStage + k_lds1;
-        const char *sv = lds + stage * kStage + v_lds;  // + 512 t for d tile t
+    auto step = [&](int j, const char *stage, bool ok0, bool ok1) {
+        const char *sk0 = stage + k_lds0;
+        const char *sk1 = stage + k_lds1;
+        const char *sv = stage + v_lds;  // + 512 t for d tile t
         const int t0 = j * kBlockTokens + 8 * q;  // lane's first token: t0 + 4T + i
         // Every token of the step attended and visible to every column of the wave.
         const bool full = ok0 && ok1 && j * kBlockTokens + 31 <= lim_lo;
@@ -422,40 +429,52 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         }
     };
 
-    // Pipeline: the loads of step i + 2 are issued when step i starts, held in
-    // registers, and written to the LDS ring after step i + 1 has computed, so
-    // global latency has two steps to hide; one barrier per step.  Stage
-    // (i + 1) % 3, written at the end of step i, was last read in step i - 2,
-    // which every wave finished before the barrier of step i - 1.
+    // Pipeline: the loads of step i + 2 are issued into stage (i + 2) % 3 when
+    // step i starts, so global latency has two steps to hide.  That stage held
+    // step i - 1, which every wave finished before the barrier that opened step
+    // i.  Before the barrier that opens step i + 1, each wave waits for its own
+    // loads of step i + 1 (only those of step i + 2, issued later, may still be
+    // in flight); after it, every wave's loads of step i + 1 are in LDS.  The
+    // waits are explicit and the barrier is s_barrier alone: __syncthreads()
+    // would also wait for the loads of step i + 2.  The empty asm statements with
+    // a memory clobber keep the compiler from moving LDS accesses across them.
     if (nsteps > 0) {
-        u32x4 stA[kLoads], stB[kLoads];
         int a0, a1, b0, b1, c0, c1;  // block ids of steps i, i + 1, i + 2
         ids(jb, a0, a1);
-        fetch(a0, a1, stA);
-        stash(0, stA);
+        dma(lds0, a0, a1);
         ids(jb + 2, b0, b1);
-        fetch(b0, b1, stB);  // past the end the loads read block 0 (never used)
-        for (int i = 0; i < nsteps; i += 2) {
-            // step i: stage i % 3; stB holds step i + 1
-            __syncthreads();
+        dma(lds1, b0, b1);  // past the end the loads read block 0 (never used)
+        auto publish = [&]() {  // own loads of the next step landed, then the barrier
+            if constexpr (kLoads == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        publish();
+        auto iteration = [&](int i, const char *cur, char *ahead) {  // step i from cur; step i + 2 into ahead
             ids(jb + 2 * (i + 2), c0, c1);
-            fetch(c0, c1, stA);
-            if (has_cols && (jb + 2 * i) * kBlockTokens <= lim_hi) step(jb + 2 * i, i % 3, a0 >= 0, a1 >= 0);
-            if (i + 1 < nsteps) {  // uniform over the workgroup
-                stash((i + 1) % 3, stB);
-                a0 = c0;
-                a1 = c1;
-                // step i + 1: stage (i + 1) % 3; stA holds step i + 2
-                __syncthreads();
-                ids(jb + 2 * (i + 3), c0, c1);
-                fetch(c0, c1, stB);
-                if (has_cols && (jb + 2 * (i + 1)) * kBlockTokens <= lim_hi)
-                    step(jb + 2 * (i + 1), (i + 1) % 3, b0 >= 0, b1 >= 0);
-                stash((i + 2) % 3, stA);  // past the end: never read
-                b0 = c0;
-                b1 = c1;
-            }
+            dma(ahead, c0, c1);
+            if (has_cols && (jb + 2 * i) * kBlockTokens <= lim_hi) step(jb + 2 * i, cur, a0 >= 0, a1 >= 0);
+            publish();
+            a0 = b0;
+            a1 = b1;
+            b0 = c0;
+            b1 = c1;
+        };
+        // Whole rounds of three, then the rest (uniform over the workgroup): every
+        // way into the loop head comes from the same stage order, which keeps the
+        // compiler's waits for each stage exact.
+        int i = 0;
+        for (; i + 2 < nsteps; i += 3) {
+            iteration(i, lds0, lds2);
+            iteration(i + 1, lds1, lds0);
+            iteration(i + 2, lds2, lds1);
         }
+        if (i < nsteps) iteration(i, lds0, lds2);
+        if (i + 1 < nsteps) iteration(i + 1, lds1, lds0);
+        // The loads issued past the last step (block 0, never read) land before
+        // the workgroup ends.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     if (!has_cols) return;
 
