@@ -59,13 +59,16 @@ METRIC = "KV GB/s read and % of HBM peak; decode-attn µs/step at 100K ctx, GQA 
 # Sources of the decode kernels (the Phase-1 kernel whose traffic profiles/ records).
 KERNEL_SRC = [os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", f)
               for f in ("pa_kernels.hip", "pa_device.h")]
+# Sources of the tiled prefill kernel.
+PREFILL_SRC = [os.path.join(ROOT, "split_kv_paged_pa_amd", "csrc", f)
+               for f in ("pa_prefill.hip", "pa_device.h")]
 
 
-def kernel_sha():
-    """Hash of the kernel sources with comments and whitespace removed: it changes
-    with the code, not with its comments."""
+def kernel_sha(paths=None):
+    """Hash of the kernel sources (by default the decode kernels) with comments and
+    whitespace removed: it changes with the code, not with its comments."""
     src = ""
-    for path in KERNEL_SRC:
+    for path in KERNEL_SRC if paths is None else paths:
         with open(path) as f:
             src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -133,7 +136,8 @@ def prefill_extra(dev, stream, dtype, kc, vc, bt, spec, S, Hq, D, q_len=2048, L=
     tiles = pa.pa_select_q_kernel(1, S, q_len, Hq, spec.num_kv_heads, dtype, L)
     return {"us": round(us, 1), "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "kernel": f"prefill_kernel<128,{tiles},single pass>" if tiles else "attend_kernel"}
+            "kernel": f"prefill_kernel<128,{tiles},single pass>" if tiles else "attend_kernel",
+            "kernel_sha": kernel_sha(PREFILL_SRC)}
 
 
 def load_traffic(workload, P):
