@@ -363,6 +363,24 @@ pa_status_t pa_decode_v2_reduce_entries(void *out, const int32_t *seq_lens, int 
                                         const void *workspace, size_t workspace_bytes,
                                         void *stream);
 
+/* Repack of token-major caches into the split layout above, for callers that
+ * store K and V as [num_blocks][num_kv_heads][block_size][head_dim] (K[t][d]
+ * and V[t][d] of slot t at [..][t][d]).  The pages gather a sequence's blocks
+ * by id and permute each into token order, leaving the in-block order to the
+ * storage layout (commit 15ef28e, "[OPT] Vectorize paged_attention_v2"); this
+ * call moves a token-major cache into the order the kernels read, bit for bit.
+ *   key_out, value_out  the key_cache / value_cache layouts above (written)
+ *   key_in, value_in    token-major caches (read only)
+ * Either pair may be NULL to skip that cache, not both; an output must not
+ * overlap its input (PA_ERR_INVALID_ARGUMENT).  block_size must be 16,
+ * head_dim a multiple of x and at most 512 (PA_ERR_UNSUPPORTED); dtype
+ * PA_DTYPE_F32 or PA_DTYPE_BF16; pointers 16-byte aligned.  num_blocks == 0
+ * enqueues nothing.  Every pointer is caller-owned device memory; the call
+ * allocates nothing and is enqueued on `stream`. */
+pa_status_t pa_cache_from_token_major(void *key_out, void *value_out, const void *key_in,
+                                      const void *value_in, int num_blocks, int num_kv_heads,
+                                      int head_dim, int block_size, pa_dtype_t dtype, void *stream);
+
 /*
  * pa_decode_v2 for callers that cannot allocate: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments as

@@ -93,8 +93,48 @@ def load_library():
     lib.pa_decode_v2_groups.restype = I
     lib.pa_decode_v2_reduce_entries.argtypes = [P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.pa_decode_v2_reduce_entries.restype = I
+    lib.pa_cache_from_token_major.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.pa_cache_from_token_major.restype = I
     _lib = lib
     return lib
+
+
+def pa_cache_from_token_major(key_out, value_out, key_in, value_in, stream=None):
+    """Token-major caches [blocks, Hkv, 16, D] into the split layout the kernels
+    read: key_out [blocks, Hkv, D/x, 16, x], value_out [blocks, Hkv, D, 16] (same
+    dtype, x = key_group(dtype)).  Either (out, in) pair may be None to skip that
+    cache.  Bit-exact data movement on the GPU."""
+    ref = key_in if key_in is not None else value_in
+    if ref is None:
+        raise ValueError("at least one of key_in / value_in is needed")
+    if ref.dtype not in _DTYPE_CODE or ref.dim() != 4 or ref.shape[2] != 16:
+        raise ValueError("token-major caches [blocks, Hkv, 16, D] of float32 or bfloat16 expected")
+    nb, Hkv, B, D = ref.shape
+    x = key_group(ref.dtype)
+    args = []
+    for name, out, inp, shape in (("key", key_out, key_in, (nb, Hkv, D // x, B, x)),
+                                  ("value", value_out, value_in, (nb, Hkv, D, B))):
+        if (out is None) != (inp is None):
+            raise ValueError(f"{name}_out and {name}_in go together")
+        if inp is None:
+            args.append((ctypes.c_void_p(0), ctypes.c_void_p(0)))
+            continue
+        if tuple(inp.shape) != (nb, Hkv, B, D) or tuple(out.shape) != shape:
+            raise ValueError(f"{name}: token-major {(nb, Hkv, B, D)} in, split layout {shape} out expected")
+        args.append((_dev(f"{name}_out", out, ref.dtype), _dev(f"{name}_in", inp, ref.dtype)))
+    _check(load_library().pa_cache_from_token_major(args[0][0], args[1][0], args[0][1], args[1][1], nb,
+                                                    Hkv, D, B, _DTYPE_CODE[ref.dtype], _stream(stream)),
+           "pa_cache_from_token_major")
+
+
+def split_layout(key_tm, value_tm, stream=None):
+    """New key / value caches in the split layout from token-major ones."""
+    nb, Hkv, B, D = key_tm.shape
+    x = key_group(key_tm.dtype)
+    k = torch.empty((nb, Hkv, D // x, B, x), dtype=key_tm.dtype, device=key_tm.device)
+    v = torch.empty((nb, Hkv, D, B), dtype=value_tm.dtype, device=value_tm.device)
+    pa_cache_from_token_major(k, v, key_tm, value_tm, stream)
+    return k, v
 
 
 def pa_status_string(status: int) -> str:

@@ -26,6 +26,7 @@ PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 # (source, flags of its own)
 SOURCES = [(os.path.join(CSRC, "pa_kernels.hip"), VGPR_FORM + PRELOAD),
            (os.path.join(CSRC, "pa_prefill.hip"), VGPR_FORM + PRELOAD),
+           (os.path.join(CSRC, "pa_repack.hip"), []),
            (os.path.join(CSRC, "pa_api.cpp"), [])]
 # Diagnostic copy of the same kernels with per-workgroup timestamps
 # (-DPA_TIMELINE, csrc/pa_timeline.h); read by bench.py --timeline only.

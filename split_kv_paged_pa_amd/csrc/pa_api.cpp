@@ -316,6 +316,36 @@ pa_status_t pa_workspace_init(void *workspace, size_t workspace_bytes, void *str
                                           static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_cache_from_token_major(void *key_out, void *value_out, const void *key_in,
+                                      const void *value_in, int num_blocks, int num_kv_heads,
+                                      int head_dim, int block_size, pa_dtype_t dtype, void *stream) {
+    if (num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_INVALID_SHAPE;
+    if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARGUMENT;
+    const int es = dtype == PA_DTYPE_BF16 ? 2 : 4;
+    if (block_size != kBlockTokens || head_dim % (16 / es) != 0 || head_dim > pa::repack_max_dim())
+        return PA_ERR_UNSUPPORTED;
+    if ((key_in == nullptr) != (key_out == nullptr) || (value_in == nullptr) != (value_out == nullptr) ||
+        (key_in == nullptr && value_in == nullptr))
+        return PA_ERR_NULL_POINTER;
+    const size_t bytes = (size_t)num_blocks * num_kv_heads * kBlockTokens * head_dim * es;
+    auto overlaps = [bytes](const void *a, const void *b) {
+        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+        return x < y + bytes && y < x + bytes;
+    };
+    for (const void *p : {static_cast<const void *>(key_out), static_cast<const void *>(value_out), key_in, value_in})
+        if (p != nullptr && !aligned16(p)) return PA_ERR_INVALID_ARGUMENT;
+    if (key_in && (overlaps(key_out, key_in) || (value_in && overlaps(key_out, value_in))))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (value_in && (overlaps(value_out, value_in) || (key_in && overlaps(value_out, key_in))))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (key_in && value_in && overlaps(key_out, value_out)) return PA_ERR_INVALID_ARGUMENT;
+    if (num_blocks == 0) return PA_OK;
+    return from_hip(pa::launch_repack(key_in, value_in, key_out, value_out, num_blocks, num_kv_heads,
+                                      head_dim, dtype == PA_DTYPE_BF16 ? pa::Dtype::BF16 : pa::Dtype::F32,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int pa_select_partition_size(int num_seqs, int num_kv_heads, int max_seq_len) {
     if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return kAutoPartition;
     int cus = compute_units();

@@ -69,6 +69,14 @@ hipError_t launch_prefill(const Problem &pb, const Partials *parts, void *out, i
                           hipStream_t stream);
 // Workgroups per kv head in grid y of launch_prefill.
 int prefill_column_groups(int group, int qlen, int nct);
+// Token-major caches [num_blocks][num_kv_heads][16][head_dim] into the split
+// layout (keys [..][head_dim / x][16][x], values [..][head_dim][16]); either
+// input / output pair may be null.  head_dim a multiple of 16 bytes' worth of
+// elements, at most repack_max_dim().
+hipError_t launch_repack(const void *key_in, const void *value_in, void *key_out, void *value_out,
+                         int num_blocks, int num_kv_heads, int head_dim, Dtype dtype,
+                         hipStream_t stream);
+int repack_max_dim();
 // V2 Phase 2: partials -> out.  Row r of sequence s holds ceil(L_s / entry_tokens)
 // valid entries.
 hipError_t launch_reduce(const int32_t *seq_lens, int num_seqs, int num_q_heads, int head_dim,

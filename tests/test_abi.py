@@ -268,3 +268,28 @@ def test_q_kernel_rule():
     assert sel(1, 1, 2048, 32, 4, f32, 8192) == 0     # fp32: the decode kernel
     assert sel(1, 1, 1, 32, 4, bf, 8192) == 0         # plain decode
     assert sel(0, 1, 512, 32, 4, bf, 8192, 24) == 0   # invalid partition size
+
+
+def test_cache_repack_rejects_before_launch():
+    """pa_cache_from_token_major: every bad argument is refused on the host."""
+    lib = pa.load_library()
+    f = lib.pa_cache_from_token_major
+    A = 0x100000  # distinct fake buffers, never dereferenced (each call fails validation
+    B = 0x200000  # or enqueues nothing)
+    C = 0x300000
+    D = 0x400000
+    ok = (A, B, C, D, 10, 4, 128, 16, 1, None)
+    assert f(A, B, C, D, 0, 4, 128, 16, 1, None) == OK           # no blocks: nothing to do
+    assert f(A, B, C, D, -1, 4, 128, 16, 1, None) == SHAPE
+    assert f(A, B, C, D, 10, 0, 128, 16, 1, None) == SHAPE
+    assert f(A, B, C, D, 10, 4, 128, 32, 1, None) == UNSUP       # block size
+    assert f(A, B, C, D, 10, 4, 12, 16, 1, None) == UNSUP        # bf16: D a multiple of 8
+    assert f(A, B, C, D, 10, 4, 6, 16, 0, None) == UNSUP         # f32: D a multiple of 4
+    assert f(A, B, C, D, 10, 4, 1024, 16, 1, None) == UNSUP      # D at most 512
+    assert f(A, B, C, D, 10, 4, 128, 16, 5, None) == ARG         # dtype
+    assert f(None, None, None, None, *ok[4:]) == NULLP           # nothing to repack
+    assert f(A, None, None, D, *ok[4:]) == NULLP                 # key_out without key_in
+    assert f(A + 8, B, C, D, *ok[4:]) == ARG                     # misaligned
+    assert f(A, B, A + 16, D, *ok[4:]) == ARG                    # key_out overlaps key_in
+    assert f(A, B, C, B + 4096, *ok[4:]) == ARG                  # value_out overlaps value_in
+    assert f(A, A + 16, C, D, *ok[4:]) == ARG                    # the two outputs overlap

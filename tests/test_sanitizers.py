@@ -38,10 +38,12 @@ def _build(out):
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-mllvm", "-amdgpu-mfma-vgpr-form"] + HOST_SAN
     objs = []
-    for src in ("pa_api.cpp", "pa_kernels.hip", "pa_prefill.hip"):
-        obj = os.path.join(out, src + ".o")
-        subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj], check=True,
-                       capture_output=True)
+    # every source of libpa_decode.so, as build.py lists them
+    sys.path.insert(0, ROOT)
+    from split_kv_paged_pa_amd import build as pa_build
+    for path, _ in pa_build.SOURCES:
+        obj = os.path.join(out, os.path.basename(path) + ".o")
+        subprocess.run([HIPCC, *flags, "-c", path, "-o", obj], check=True, capture_output=True)
         objs.append(obj)
     lib = os.path.join(out, "libpa_decode_san.so")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib],
