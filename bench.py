@@ -378,6 +378,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
+    ap.add_argument("--rates", action="store_true",
+                    help="print the instruction-rate probe (libpa_probe.so) as JSON and exit")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other partition sizes and V1 (for short profiling passes)")
     ap.add_argument("--extras", action="store_true",
@@ -400,6 +402,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.rates:
+        from split_kv_paged_pa_amd import probe
+        print(json.dumps({"instruction_rates": probe.issue_rates(),
+                          "device": torch.cuda.get_device_name(dev)}))
+        return
 
     if args.dispatch_sweep:
         dispatch_sweep(dev)

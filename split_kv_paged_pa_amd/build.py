@@ -32,7 +32,8 @@ SOURCES = [(os.path.join(CSRC, "pa_kernels.hip"), VGPR_FORM + PRELOAD),
 # (-DPA_TIMELINE, csrc/pa_timeline.h); read by bench.py --timeline only.
 TIMELINE_LIB = os.path.join(HERE, "libpa_decode_timeline.so")
 PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
-PROBE_SOURCES = [(os.path.join(CSRC, "pa_probe.hip"), VGPR_FORM)]
+PROBE_SOURCES = [(os.path.join(CSRC, "pa_probe.hip"), VGPR_FORM),
+                 (os.path.join(CSRC, "pa_rates.hip"), [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 OBJ_DIR = os.path.join(HERE, "_build")
 

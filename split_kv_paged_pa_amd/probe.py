@@ -1,5 +1,6 @@
 """Binding of libpa_probe.so: an HBM read-bandwidth probe with the decode
-kernels' access shape (measurement only; not part of the attention ABI)."""
+kernels' access shape, and an instruction-rate probe (measurement only; not
+part of the attention ABI)."""
 import ctypes
 import os
 
@@ -19,6 +20,8 @@ def _load():
         P, I = ctypes.c_void_p, ctypes.c_int
         lib.pa_probe_read.argtypes = [P, P, I, I, I, I, I, P, P]
         lib.pa_probe_read.restype = I
+        lib.pa_probe_rates.argtypes = [I, I, P, I, I, I, P]
+        lib.pa_probe_rates.restype = I
         _lib = lib
     return _lib
 
@@ -52,3 +55,38 @@ def read_bandwidth(buf: torch.Tensor, chunk_ids, chunk_bytes=4096, waves_per_gro
     torch.cuda.synchronize()
     sec = e0.elapsed_time(e1) * 1e-3 / reps
     return n * chunk_bytes / sec / 1e9
+
+
+RATE_KINDS = {0: "v_exp_f32", 1: "v_fma_f32", 2: "v_mfma_f32_16x16x32_bf16",
+              3: "mfma + 3 independent fma", 4: "ds_read_b128 (8 then wait)"}
+_RATE_INSTRS = {0: 8, 1: 8, 2: 8, 3: 32, 4: 8}  # instructions per round
+
+
+def issue_rates(iters=4000, blocks=256):
+    """Cycles per instruction per wave for each instruction stream of
+    pa_rates.hip: one wave per SIMD (256 threads, one workgroup per CU), two
+    waves of the same stream, and two waves of different streams sharing each
+    SIMD (waves w and w + 4 of 512 threads).  Returns a list of rows
+    {"lo", "hi", "threads", "clock_ghz", "lo_cycles_per_instr", "hi_cycles_per_instr"}."""
+    import numpy as np
+    lib = _load()
+    rows = []
+    pairs = [(k, k, t) for k in range(5) for t in (256, 512)] + [(2, 1, 512), (2, 0, 512), (2, 4, 512)]
+    for lo, hi, threads in pairs:
+        waves = blocks * threads // 64
+        out = torch.zeros(waves * 3, dtype=torch.int64, device="cuda")
+        st = torch.cuda.current_stream()
+        assert lib.pa_probe_rates(lo, hi, ctypes.c_void_p(out.data_ptr()), blocks, threads, iters,
+                                  ctypes.c_void_p(st.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().reshape(waves, 3).astype(np.float64)
+        cyc, rt = o[:, 0], o[:, 1]
+        per_wg = threads // 64
+        idx = np.arange(waves) % per_wg
+        row = {"lo": RATE_KINDS[lo], "hi": RATE_KINDS[hi], "threads": threads,
+               "clock_ghz": round(float(np.median(cyc / rt)) * 0.1, 3),
+               "lo_cycles_per_instr": round(float(np.median(cyc[(idx & 4) == 0])) / (iters * _RATE_INSTRS[lo]), 2)}
+        if threads == 512:
+            row["hi_cycles_per_instr"] = round(float(np.median(cyc[(idx & 4) != 0])) / (iters * _RATE_INSTRS[hi]), 2)
+        rows.append(row)
+    return rows
