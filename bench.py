@@ -380,6 +380,9 @@ def main():
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--rates", action="store_true",
                     help="print the instruction-rate probe (libpa_probe.so) as JSON and exit")
+    ap.add_argument("--lds-banks", action="store_true",
+                    help="print the LDS read-pattern probe (libpa_probe.so) as JSON and exit: "
+                         "one dispatch per lane pattern, in the printed order")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other partition sizes and V1 (for short profiling passes)")
     ap.add_argument("--extras", action="store_true",
@@ -406,6 +409,11 @@ def main():
     if args.rates:
         from split_kv_paged_pa_amd import probe
         print(json.dumps({"instruction_rates": probe.issue_rates(),
+                          "device": torch.cuda.get_device_name(dev)}))
+        return
+    if args.lds_banks:
+        from split_kv_paged_pa_amd import probe
+        print(json.dumps({"lds_pattern_clocks": probe.lds_pattern_rates(),
                           "device": torch.cuda.get_device_name(dev)}))
         return
 

@@ -11,6 +11,11 @@
 // Waves 0-3 of a workgroup run kind `lo`, waves 4-7 kind `hi`; with 512 threads
 // waves w and w + 4 share a SIMD.  All instruction streams are written as asm
 // so that the counts are exact; the LDS reads wait in the same asm block.
+//
+// A second kernel reads LDS with a caller-given 16-byte offset per lane (the
+// same 64 offsets in every wave), to measure which lane patterns of a 128-bit
+// LDS read conflict: its clocks per read, and the LDS bank-conflict counter of
+// its dispatch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,7 +114,52 @@ int launch_rate(void *out, int blocks, int threads, int iters, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+constexpr int kPatternLds = 32768;              // bytes of LDS the pattern kernel reads
+constexpr int kPatternSpan = 7 * 1024 + 16;      // bytes one lane's 8 reads cover past its offset
+constexpr int kPatternMaxOffset = kPatternLds - kPatternSpan;
+
+// 256 threads (one wave per SIMD); per round each wave issues 8 ds_read_b128 at
+// its lane's offset + 1024 k, then waits.  Offsets are clamped into the array
+// and rounded down to 16 bytes, so every read stays inside it.
+__global__ __launch_bounds__(256) void lds_pattern_kernel(const int *__restrict__ offsets,
+                                                         unsigned long long *__restrict__ out, int iters) {
+    __shared__ __attribute__((aligned(16))) char lds[kPatternLds];
+    for (int i = threadIdx.x; i < kPatternLds / 4; i += blockDim.x) reinterpret_cast<uint32_t *>(lds)[i] = i;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    const int off = min(max(offsets[threadIdx.x & 63], 0), kPatternMaxOffset) & ~15;
+    const unsigned base = (unsigned)(uintptr_t)(lds + off);
+    uint32_t acc = 0;
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int i = 0; i < iters; ++i) {
+        uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+        asm volatile(
+            "ds_read_b128 %0, %8\n ds_read_b128 %1, %8 offset:1024\n ds_read_b128 %2, %8 offset:2048\n"
+            "ds_read_b128 %3, %8 offset:3072\n ds_read_b128 %4, %8 offset:4096\n ds_read_b128 %5, %8 offset:5120\n"
+            "ds_read_b128 %6, %8 offset:6144\n ds_read_b128 %7, %8 offset:7168\n s_waitcnt lgkmcnt(0)"
+            : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3), "=v"(v4), "=v"(v5), "=v"(v6), "=v"(v7)
+            : "v"(base));
+        acc ^= v0.x ^ v1.y ^ v2.z ^ v3.w ^ v4.x ^ v5.y ^ v6.z ^ v7.w;
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    if ((threadIdx.x & 63) == 0) {
+        const unsigned w = blockIdx.x * 4 + wave;
+        out[2 * w + 0] = t1 - t0;
+        out[2 * w + 1] = acc;
+    }
+}
+
 }  // namespace
+
+// offsets: 64 ints in device memory, the byte offset each lane reads at (clamped
+// to [0, 32768 - 7 * 1024 - 16], rounded down to 16).  out: 2 * 4 * blocks u64
+// records {shader clocks, sink} per wave.  Returns 0, or -1 for bad arguments.
+extern "C" int pa_probe_lds_pattern(const void *offsets, void *out, int blocks, int iters, void *stream) {
+    if (offsets == nullptr || out == nullptr || blocks <= 0 || iters <= 0) return -1;
+    hipLaunchKernelGGL(lds_pattern_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const int *>(offsets), static_cast<unsigned long long *>(out), iters);
+    return (int)hipGetLastError();
+}
 
 // out: 3 * blocks * threads / 64 u64 records.  threads 256 or 512; (lo, hi) one of
 // the pairs below, else -1.

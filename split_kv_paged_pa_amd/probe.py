@@ -1,6 +1,6 @@
 """Binding of libpa_probe.so: an HBM read-bandwidth probe with the decode
-kernels' access shape, and an instruction-rate probe (measurement only; not
-part of the attention ABI)."""
+kernels' access shape, an instruction-rate probe and an LDS read-pattern probe
+(measurement only; not part of the attention ABI)."""
 import ctypes
 import os
 
@@ -22,6 +22,8 @@ def _load():
         lib.pa_probe_read.restype = I
         lib.pa_probe_rates.argtypes = [I, I, P, I, I, I, P]
         lib.pa_probe_rates.restype = I
+        lib.pa_probe_lds_pattern.argtypes = [P, P, I, I, P]
+        lib.pa_probe_lds_pattern.restype = I
         _lib = lib
     return _lib
 
@@ -89,4 +91,76 @@ def issue_rates(iters=4000, blocks=256):
         if threads == 512:
             row["hi_cycles_per_instr"] = round(float(np.median(cyc[(idx & 4) != 0])) / (iters * _RATE_INSTRS[hi]), 2)
         rows.append(row)
+    return rows
+
+
+def _bits_pattern(bits):
+    """Lane l reads 16-byte slot (lane bits `bits`, packed) of 256-byte line
+    (the other two lane bits, packed): the 16 lanes of a group read 16 distinct
+    slots exactly when the group's lanes vary in the bits `bits` and agree in
+    the other two."""
+    rest = [b for b in range(6) if b not in bits]
+    offs = []
+    for lane in range(64):
+        slot = sum(((lane >> b) & 1) << i for i, b in enumerate(bits))
+        line = sum(((lane >> b) & 1) << i for i, b in enumerate(rest))
+        offs.append(256 * line + 16 * slot)
+    return offs
+
+
+def _prefill_pattern(kind):
+    """The per-lane LDS offsets of the tiled prefill's operand reads at D = 128
+    (lane = n + 16 q; regions 4096 + 128 bytes apart): key tile 0 and 1, values
+    in slab order, and values under the earlier permutation (token-half bit
+    flipped by bits 3 and 4 of the piece index)."""
+    region = 4096 + 128
+    offs = []
+    for lane in range(64):
+        n, q = lane & 15, lane >> 4
+        kb = (n >> 2) & 1
+        if kind == "k0":
+            o = (n >> 3) * region + q * 256 + (12 * kb + (n & 3)) * 16
+        elif kind == "k1":
+            o = (n >> 3) * region + q * 256 + (8 * kb + 4 * (1 - kb) + (n & 3)) * 16
+        else:
+            x = 2 * n + (q & 1)
+            if kind == "v_permuted":
+                x ^= ((x >> 3) ^ (x >> 4)) & 1
+            o = (q >> 1) * region + x * 16
+        offs.append(o)
+    return offs
+
+
+def lds_patterns():
+    """Named 64-lane offset patterns for `lds_pattern_rates`, in run order."""
+    import itertools
+    pats = {"linear": [16 * l for l in range(64)],
+            "stride256": [256 * (l % 16) + 16 * (l // 16) for l in range(64)]}
+    for bits in itertools.combinations(range(6), 4):
+        pats["bits" + "".join(map(str, bits))] = _bits_pattern(bits)
+    for kind in ("k0", "k1", "v", "v_permuted"):
+        pats["prefill_" + kind] = _prefill_pattern(kind)
+    for name, offs in pats.items():
+        assert len(offs) == 64 and all(0 <= o <= 32768 - 7 * 1024 - 16 and o % 16 == 0 for o in offs), name
+    return pats
+
+
+def lds_pattern_rates(iters=2000, blocks=256):
+    """Clocks per ds_read_b128 per wave for each pattern of lds_patterns(), one
+    dispatch per pattern in that order (4 waves per CU, all reading the same
+    lane pattern).  A conflict-free 128-bit read takes 4 clocks of the CU's LDS
+    (16 per read per wave with 4 waves sharing it); each round of 8 reads also
+    waits out the LDS latency once, so conflict-free patterns measure above 16."""
+    import numpy as np
+    lib = _load()
+    rows = []
+    st = torch.cuda.current_stream()
+    for name, offs in lds_patterns().items():
+        dev = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        out = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device="cuda")
+        assert lib.pa_probe_lds_pattern(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                        blocks, iters, ctypes.c_void_p(st.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        cyc = out.cpu().numpy().reshape(-1, 2)[:, 0].astype(np.float64)
+        rows.append({"pattern": name, "clocks_per_read": round(float(np.median(cyc)) / (iters * 8), 2)})
     return rows
