@@ -114,28 +114,41 @@ def prefill_extra(dev, stream, dtype, kc, vc, bt, spec, S, Hq, D, q_len=2048, L=
     """q_len query tokens per sequence over the first L tokens of the workload's
     cache through pa_decode_v1_q (which takes the tiled prefill kernel at this
     size): microseconds per call and MFMA throughput, 4 * D flops per visible
-    (query token, head, cache token)."""
+    (query token, head, cache token).
+
+    The first calls after other work run slower: on MI355X this kernel took ~300 us
+    per call over its first 50 calls after an idle spell and ~221 us per call from
+    then on (sysfs showed the board power climbing from ~0.3 to ~1 kW meanwhile,
+    under its 1.4 kW cap).  So `us` is the mean of 50 calls after 100 untimed ones;
+    `us_after_3` keeps the mean of the 10 calls that follow the first 3."""
     qp = torch.randn(S, q_len, Hq, D, device=dev).to(dtype)
     op = torch.empty_like(qp)
     slp = torch.full((S,), L, dtype=torch.int32, device=dev)
 
     def run():
         pa.pa_decode_v1_q(op, qp, kc, vc, bt, slp, spec.scale, L)
+
+    def timed(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
     for _ in range(3):
         run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
+    us_short = timed(10)
+    for _ in range(100 - 13):
         run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / 10
+    us = timed(50)
     pairs = S * Hq * sum(L - q_len + j + 1 for j in range(q_len))
     tflops = 4.0 * D * pairs / (us * 1e-6) / 1e12
     tiles = pa.pa_select_q_kernel(1, S, q_len, Hq, spec.num_kv_heads, dtype, L)
     return {"us": round(us, 1), "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "us_after_3": round(us_short, 1),
+            "calls": "100 untimed, then 50 timed",
             "kernel": f"prefill_kernel<128,{tiles},single pass>" if tiles else "attend_kernel",
             "kernel_sha": kernel_sha(PREFILL_SRC)}
 
