@@ -58,9 +58,6 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-// Staging registers: a native vector (plain loads and stores; HIP's uint4 is a
-// struct whose copies through an array stay in scratch memory).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPrefillWaves = 4;
 // A column's reference max moves when a logit exceeds it by more than this (log2 units).

@@ -285,6 +285,8 @@ FUSED = [  # name, dtype, Hq, Hkv, D, lens, P
     ("grouped_long", "bf16", 64, 8, 128, [20000], 512),
     ("g16_d128", "bf16", 16, 1, 128, [9000, 33], 64),
     ("long_100k_shape", "bf16", 32, 4, 128, [100000], 1024),
+    # 8 x 4 rows x 36 partitions: several partitions per workgroup, folded.
+    ("partitions", "bf16", 32, 4, 128, [9000, 8000, 7000, 100, 9000, 1, 5000, 9000], 256),
 ]
 
 
