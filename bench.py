@@ -513,8 +513,11 @@ def main():
     def form_line(run, n):
         """Per-step statistics of one form (an event pair per step, so each step
         also carries the pair's own overhead), then the mean of n steps run back
-        to back between one event pair, as the headline value is taken."""
-        for i in range(5 if n > 5 else 1):
+        to back between one event pair, as the headline value is taken.  A V2 form
+        first runs 100 untimed steps: after V1, which leaves most of the GPU idle,
+        the step takes ~60 steps to come back to its steady time (measured on
+        MI355X: 38.7 us per step over the first 20, 36.6-36.8 us from the 60th)."""
+        for i in range(100 if n > 5 else 1):
             run(i)
         st = step_stats(time_per_step(run, n, stream))
         st["gb_per_s"] = round(spec.kv_bytes / (st["median"] * 1e-6) / 1e9, 1)
