@@ -396,6 +396,9 @@ def main():
     ap.add_argument("--lds-banks", action="store_true",
                     help="print the LDS read-pattern probe (libpa_probe.so) as JSON and exit: "
                          "one dispatch per lane pattern, in the printed order")
+    ap.add_argument("--xcd-probe", action="store_true",
+                    help="print the per-XCD read timing of the HBM probe (libpa_probe.so) as JSON "
+                         "and exit")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other partition sizes and V1 (for short profiling passes)")
     ap.add_argument("--extras", action="store_true",
@@ -422,6 +425,11 @@ def main():
     if args.rates:
         from split_kv_paged_pa_amd import probe
         print(json.dumps({"instruction_rates": probe.issue_rates(),
+                          "device": torch.cuda.get_device_name(dev)}))
+        return
+    if args.xcd_probe:
+        from split_kv_paged_pa_amd import probe
+        print(json.dumps({"xcd_read": probe.xcd_read_rates(),
                           "device": torch.cuda.get_device_name(dev)}))
         return
     if args.lds_banks:

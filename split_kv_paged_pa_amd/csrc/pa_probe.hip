@@ -17,6 +17,11 @@
 // The chunks are split evenly over num_groups workgroups of waves_per_group
 // waves; sink receives one uint32 per thread (num_groups * waves_per_group * 64).
 // Returns 0 on success, 1 for invalid arguments, 2 for a failed launch.
+//
+//   pa_probe_read_xcd(..., sink, times, stream)
+// The same with shape 0, plus three uint64 per workgroup in `times`: the 100 MHz
+// constant clock when its wave 0 starts and when it has folded its last chunk,
+// and the XCC (XCD) id it ran on -- to compare the XCDs' read rates.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,7 +40,9 @@ template <int NC, int SHAPE>
 __global__ __launch_bounds__(1024) void probe_kernel(const uint4 *__restrict__ base,
                                                      const int32_t *__restrict__ chunk_ids,
                                                      int num_chunks, int chunks_per_group,
-                                                     uint32_t *__restrict__ sink) {
+                                                     uint32_t *__restrict__ sink,
+                                                     unsigned long long *__restrict__ times) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
@@ -64,6 +71,13 @@ __global__ __launch_bounds__(1024) void probe_kernel(const uint4 *__restrict__ b
             for (int c = 0; c < NC; ++c) acc ^= r[u][c][0] ^ r[u][c][1] ^ r[u][c][2] ^ r[u][c][3];
     }
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+    if (times != nullptr && threadIdx.x == 0) {
+        // XCC_ID: hardware register 20, bits 0-3.
+        const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u;
+        times[3 * blockIdx.x + 0] = t0;
+        times[3 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+        times[3 * blockIdx.x + 2] = xcc;
+    }
 }
 
 }  // namespace
@@ -80,14 +94,26 @@ extern "C" int pa_probe_read(const void *base, const int32_t *chunk_ids, int num
     const uint4 *b = static_cast<const uint4 *>(base);
     uint32_t *o = static_cast<uint32_t *>(sink);
     if (shape == 1) {
-        probe_kernel<4, 1><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o);
+        probe_kernel<4, 1><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o, nullptr);
         return hipGetLastError() == hipSuccess ? 0 : 2;
     }
     switch (chunk_bytes) {
-        case 1024: probe_kernel<1, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o); break;
-        case 4096: probe_kernel<4, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o); break;
-        case 16384: probe_kernel<16, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o); break;
+        case 1024: probe_kernel<1, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o, nullptr); break;
+        case 4096: probe_kernel<4, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o, nullptr); break;
+        case 16384: probe_kernel<16, 0><<<grid, block, 0, s>>>(b, chunk_ids, num_chunks, per, o, nullptr); break;
         default: return 1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int pa_probe_read_xcd(const void *base, const int32_t *chunk_ids, int num_chunks,
+                                 int chunk_bytes, int waves_per_group, int num_groups, void *sink,
+                                 void *times, void *stream) {
+    if (!base || !sink || !times || num_chunks <= 0 || num_groups <= 0) return 1;
+    if (waves_per_group < 1 || waves_per_group > 16 || chunk_bytes != 4096) return 1;
+    const int per = (num_chunks + num_groups - 1) / num_groups;
+    probe_kernel<4, 0><<<dim3(num_groups), dim3(waves_per_group * 64), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint4 *>(base), chunk_ids, num_chunks, per, static_cast<uint32_t *>(sink),
+        static_cast<unsigned long long *>(times));
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }

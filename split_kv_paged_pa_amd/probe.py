@@ -24,6 +24,8 @@ def _load():
         lib.pa_probe_rates.restype = I
         lib.pa_probe_lds_pattern.argtypes = [P, P, I, I, P]
         lib.pa_probe_lds_pattern.restype = I
+        lib.pa_probe_read_xcd.argtypes = [P, P, I, I, I, I, P, P, P]
+        lib.pa_probe_read_xcd.restype = I
         _lib = lib
     return _lib
 
@@ -164,3 +166,41 @@ def lds_pattern_rates(iters=2000, blocks=256):
         cyc = out.cpu().numpy().reshape(-1, 2)[:, 0].astype(np.float64)
         rows.append({"pattern": name, "clocks_per_read": round(float(np.median(cyc)) / (iters * 8), 2)})
     return rows
+
+
+def xcd_read_rates(gib=4, chunks=50_000, groups=256, waves=4, reps=12, seed=5):
+    """Per-XCD read timing of the read probe: each launch reads `chunks` random
+    4 KiB chunks of a `gib` GiB buffer (as many as the 100K-token decode step
+    reads), a set disjoint from the previous launches' sets (so no cache holds
+    them), split evenly over `groups` workgroups of `waves` waves (one per CU).
+    Returns the launches' mean duration and, per XCC id, the mean time (us) from
+    a launch's first workgroup start to its workgroups' ends, over all launches
+    and for each launch."""
+    import numpy as np
+    lib = _load()
+    nbytes = gib << 30
+    nsets = (nbytes // 4096) // chunks
+    assert nsets >= reps + 1, "the buffer holds too few disjoint chunk sets"
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    perm = np.random.default_rng(seed).permutation(nbytes // 4096).astype(np.int32)
+    sink = torch.empty(groups * waves * 64, dtype=torch.int32, device="cuda")
+    times = torch.zeros(groups * 3, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream()
+    runs = []
+    for r in range(reps + 1):
+        ids = torch.from_numpy(perm[r * chunks:(r + 1) * chunks].copy()).cuda()
+        assert lib.pa_probe_read_xcd(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(ids.data_ptr()),
+                                     chunks, 4096, waves, groups, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(times.data_ptr()), ctypes.c_void_p(st.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        if r == 0:
+            continue  # warm-up launch
+        t = times.cpu().numpy().reshape(groups, 3).astype(np.float64)
+        t0 = t[:, 0].min()
+        runs.append(((t[:, 1] - t0) / 100.0, t[:, 2].astype(int)))
+    xccs = sorted(set(runs[0][1].tolist()))
+    per_run = [{int(x): round(float(e[c == x].mean()), 2) for x in xccs} for e, c in runs]
+    kernel_us = float(np.mean([e.max() for e, _ in runs]))
+    return {"kernel_us": round(kernel_us, 2), "gb_per_s": round(chunks * 4096 / (kernel_us * 1e-6) / 1e9, 1),
+            "end_us_mean_by_xcc": {int(x): round(float(np.mean([p[x] for p in per_run])), 2) for x in xccs},
+            "end_us_by_xcc_per_launch": per_run}
