@@ -42,6 +42,39 @@ def test_small_ragged(dtype, D, Hq, Hkv, variant, P):
     assert_close(to_f64(out), ref, dtype, f"{variant} P={P}")
 
 
+# fp32 stops at 0.3: at scale 2.0 (logits of magnitude ~50 at D = 128) the fp32
+# rounding of q.k alone, about sqrt(D) * 2^-24 * |scale| * sum |q_d k_d|, moves
+# the weights by ~1e-5 -- the fp32 bar, which is derived for scales near
+# 1 / sqrt(D) (measured 1.5e-5 there; bf16's bar covers it).
+SCALES = [("bf16", -0.11), ("bf16", 0.0), ("bf16", 0.3), ("bf16", 2.0),
+          ("f32", -0.11), ("f32", 0.0), ("f32", 0.3)]
+
+
+@pytest.mark.parametrize("dtype,scale", SCALES, ids=[f"{d}_{s}" for d, s in SCALES])
+def test_decode_scale_values(dtype, scale):
+    """Negative, zero, large and non-default positive scales through V1, V2 (per
+    partition and equal spans), the single launch and q_len 3 on the decode
+    kernel: the logits are scale * q.k before the max, whatever its sign."""
+    spec = wl.custom(f"scale_{dtype}", 151, dtype, 32, 4, 128, [3000, 17, 1500], scale=scale)
+    b = wl.generate(spec)
+    db = DeviceBatch(b)
+    print(f"[case] decode scale={scale} {dtype}", flush=True)
+    ref = oracle_out(b)
+    assert_close(to_f64(db.run_v1()), ref, dtype, f"v1 scale={scale}")
+    for P in (64, 512):
+        assert_close(to_f64(db.run_v2(P)), ref, dtype, f"v2 P={P} scale={scale}")
+    out = db.new_out()
+    pa.pa_decode_v2_single(out, *db.args(), 256, db.workspace(256))
+    assert_close(to_f64(out), ref, dtype, f"single launch scale={scale}")
+    q = _multi_query(spec, 3)
+    _, kc, vc, bt, sl = b.numpy()
+    refq = oracle.decode_q(wl.to_numpy(q.cpu()), kc, vc, bt, sl, scale, dtype=dtype)
+    outq = torch.full_like(q, float("nan"))
+    pa.pa_decode_v1_q(outq, q, db.key_cache, db.value_cache, db.block_tables, db.seq_lens, scale,
+                      db.max_seq_len)
+    assert_close(to_f64(outq), refq, dtype, f"v1_q q_len=3 scale={scale}")
+
+
 def test_zero_length_rows_are_zero():
     spec = wl.custom("zeros", 102, "bf16", 8, 2, 128, [0, 40, 0])
     db = DeviceBatch(wl.generate(spec))
