@@ -221,7 +221,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // so the sums cost no VALU additions and use the very weights the output
     // does.
     f32x4 accl[NCT];
-    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0
+    uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0
+    // Opaque to the compiler, so the operand stays in four VGPRs instead of being
+    // rebuilt from scalar registers (two v_mov_b64) in every step; measured on
+    // MI355X, same-box A/B: q_len 2048 -0.4 to -0.8%, bitwise-identical.
+    asm volatile("" : "+v"(ones.x), "+v"(ones.y), "+v"(ones.z), "+v"(ones.w));
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         m[ct] = -INFINITY;
