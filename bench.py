@@ -640,6 +640,10 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2), "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        # The two clocks of the timed region (ms_per_step is the larger): the wall
+        # clock carries a fixed ~16 us of first launch into an idle queue and
+        # completion signalling per timed run, ~0.8 us per step at K = 20.
+        "us_per_step_wall": round(ms_wall * 1e3, 2), "us_per_step_events": round(ms_event * 1e3, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
         "data": f"synthetic (seeded N(0,1) {spec.dtype} keys/values/query, random block permutation)",
         "config": {"workload": spec.name, "num_seqs": S, "seq_len": int(spec.seq_lens.max()),
